@@ -1,0 +1,618 @@
+// C ABI of the block-sparse attention library: request validation, the
+// online request path (mask state -> statistics transfer -> regime lookup and
+// ranked fallback -> launch preparation), plan lifetime and kernel dispatch.
+//
+// Tessera paper, section 3 "Online request path" and section 5.2 "Online
+// Plan Selection": the runtime builds the shared mask state on the GPU,
+// transfers only its scalar statistics to the host, selects the first
+// eligible plan of the regime's ranking (the key's base plan on a lookup
+// miss), derives only that plan's metadata from the block-CSR, binds the
+// temporary workspace and invokes the plan's kernels.
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/bsa.h"
+#include "bsa_internal.h"
+#include "catalog.h"
+
+using namespace bsa;
+
+namespace {
+
+thread_local std::string g_err;
+
+bsa_status fail(bsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                        \
+  do {                                                                                       \
+    hipError_t e_ = (expr);                                                                  \
+    if (e_ != hipSuccess)                                                                    \
+      return fail(BSA_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, \
+                  __LINE__);                                                                 \
+  } while (0)
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- device memory cache ------------------------------------------------------
+// Plans come and go once per request; the cache keeps freed device blocks per
+// (device, size class) so steady-state requests make no hipMalloc calls.
+struct Pool {
+  std::mutex mu;
+  std::map<std::pair<int, size_t>, std::vector<void*>> free;
+  size_t idle = 0;
+  static constexpr size_t kIdleCap = size_t(16) << 30;
+};
+Pool g_pool;
+
+size_t size_class(size_t bytes) {
+  if (bytes <= 65536) return 65536;
+  size_t p = 65536;
+  while (p < bytes) p <<= 1;
+  // eight classes per octave
+  const size_t step = p / 16;
+  return ((bytes + step - 1) / step) * step;
+}
+
+struct DevBuf {
+  void* ptr = nullptr;
+  size_t cap = 0;
+  int dev = -1;
+};
+
+hipError_t pool_alloc(int dev, size_t bytes, DevBuf* b) {
+  const size_t cap = size_class(bytes ? bytes : 1);
+  {
+    std::lock_guard<std::mutex> lk(g_pool.mu);
+    auto it = g_pool.free.find({dev, cap});
+    if (it != g_pool.free.end() && !it->second.empty()) {
+      b->ptr = it->second.back();
+      it->second.pop_back();
+      g_pool.idle -= cap;
+      b->cap = cap;
+      b->dev = dev;
+      return hipSuccess;
+    }
+  }
+  hipError_t e = hipMalloc(&b->ptr, cap);
+  if (e != hipSuccess) return e;
+  b->cap = cap;
+  b->dev = dev;
+  return hipSuccess;
+}
+
+void pool_release(DevBuf* b) {
+  if (!b->ptr) return;
+  std::lock_guard<std::mutex> lk(g_pool.mu);
+  if (g_pool.idle + b->cap > Pool::kIdleCap) {
+    (void)hipFree(b->ptr);
+  } else {
+    g_pool.free[{b->dev, b->cap}].push_back(b->ptr);
+    g_pool.idle += b->cap;
+  }
+  b->ptr = nullptr;
+}
+
+// pinned host staging for the statistics transfer, one per thread
+MaskStats* pinned_stats() {
+  thread_local MaskStats* p = nullptr;
+  if (!p) {
+    if (hipHostMalloc((void**)&p, sizeof(MaskStats), hipHostMallocDefault) != hipSuccess) p = nullptr;
+  }
+  return p;
+}
+
+int device_cus(int dev) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev] = n;
+  return n;
+}
+
+int wg_per_cu_cached(int tq, int tkv, int d) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  const int key = (tq << 20) | (tkv << 8) | d;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = attn_wg_per_cu(tq, tkv, d);
+  if (n <= 0) n = 1;
+  cache[key] = n;
+  return n;
+}
+
+// Split-K rule of the "balance" organization: a query tile's traversal is cut
+// when it holds more entries than the even share of all entries over the
+// resident workgroup slots of the device (at least 4 entries per partition).
+struct PlanShape {
+  DimMap mq, mk;
+  int split = 0;           // entries per partition, 0 = never split
+  int64_t tasks_upper = 0;
+  int64_t slots_upper = 0;
+  int64_t ws_bytes = 0;
+  int64_t nqt = 0;
+  int nqt_head = 0;
+};
+
+PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStats& st, int dev) {
+  PlanShape p;
+  p.mq = map_dim(r.block_q, e.tq, 32);
+  p.mk = map_dim(r.block_kv, e.tkv, 1);
+  p.nqt_head = (int)cdiv(r.N, e.tq);
+  p.nqt = (int64_t)r.H * p.nqt_head;
+  // entries visited over all query tiles (upper bound for coarsened lists)
+  const int64_t W = (int64_t)p.mq.refine * (int64_t)st.nnz;
+  const int64_t row_max = (int64_t)p.mq.coarsen * st.max_row_nnz;
+  int split = 0;
+  if (r.force_split > 0) {
+    split = r.force_split;
+  } else if (r.force_split < 0 && e.split) {
+    const int64_t slots = (int64_t)device_cus(dev) * wg_per_cu_cached(e.tq, e.tkv, e.d);
+    split = (int)std::max<int64_t>(4, cdiv(std::max<int64_t>(W, 1), slots));
+    if (row_max <= split) split = 0;
+  }
+  p.split = split;
+  if (split > 0) {
+    p.tasks_upper = p.nqt + W / split + 1;
+    p.slots_upper = 2 * W / split + 1;
+  } else {
+    p.tasks_upper = p.nqt;
+    p.slots_upper = 0;
+  }
+  p.ws_bytes = p.slots_upper * (int64_t)e.tq * (e.d + 2) * 4;
+  return p;
+}
+
+}  // namespace
+
+struct bsa_plan {
+  bsa_request req{};
+  int dev = 0;
+  int nqb = 0, nkb = 0;
+  const CatalogEntry* entry = nullptr;
+  PlanShape shape;
+  int ntr = 0;  // tile-list rows per head
+  int64_t grid = 0;
+  bool coarse = false;
+  MaskStats stats{};
+  bsa_plan_info info{};
+  DevBuf stats_dev, row_cnt, row_ptr, cols, trow_cnt, trow_ptr_buf, tcol_buf, tbits_buf, parts, slots,
+      task_off, slot_off, tasks, ws;
+  const int32_t* trow_ptr = nullptr;
+  const int32_t* tcol = nullptr;
+  const uint32_t* tbits = nullptr;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+
+  ~bsa_plan() {
+    for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &cols, &trow_cnt, &trow_ptr_buf, &tcol_buf,
+                      &tbits_buf, &parts, &slots, &task_off, &slot_off, &tasks, &ws})
+      pool_release(b);
+    for (auto& e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+};
+
+namespace {
+
+bsa_status validate_request(const bsa_request* r) {
+  if (!r) return fail(BSA_ERR_INVALID_ARG, "request is NULL");
+  if (r->H < 1 || r->N < 1) return fail(BSA_ERR_INVALID_ARG, "H and N must be >= 1 (H=%d N=%d)", r->H, r->N);
+  if (!r->mask) return fail(BSA_ERR_INVALID_ARG, "mask pointer is NULL");
+  if (r->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_UNSUPPORTED, "dtype %d unsupported (bf16 only)", r->dtype);
+  if (r->layout != BSA_LAYOUT_HND) return fail(BSA_ERR_UNSUPPORTED, "layout %d unsupported", r->layout);
+  if (r->d != 64 && r->d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim %d unsupported (64, 128)", r->d);
+  if (!pow2(r->block_q) || r->block_q < 16 || r->block_q > 256)
+    return fail(BSA_ERR_UNSUPPORTED, "block_q %d unsupported (power of two in [16, 256])", r->block_q);
+  if (!pow2(r->block_kv) || r->block_kv < 16 || r->block_kv > 256)
+    return fail(BSA_ERR_UNSUPPORTED, "block_kv %d unsupported (power of two in [16, 256])", r->block_kv);
+  const int64_t nqb = cdiv(r->N, r->block_q), nkb = cdiv(r->N, r->block_kv);
+  if ((int64_t)r->H * nqb * nkb >= (int64_t(1) << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "mask has %lld blocks (limit 2^31)", (long long)((int64_t)r->H * nqb * nkb));
+  if ((int64_t)r->H * r->N >= (int64_t(1) << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "H*N too large");
+  if (r->force_plan >= (int)catalog().size() || r->force_plan < -1)
+    return fail(BSA_ERR_INVALID_ARG, "force_plan %d out of range", r->force_plan);
+  if (r->force_split < -1) return fail(BSA_ERR_INVALID_ARG, "force_split %d invalid", r->force_split);
+  if (r->workspace_limit < 0) return fail(BSA_ERR_INVALID_ARG, "negative workspace limit");
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_status_string(int32_t s) {
+  switch (s) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_ERR_INVALID_ARG: return "BSA_ERR_INVALID_ARG";
+    case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+    case BSA_ERR_NO_MEMORY: return "BSA_ERR_NO_MEMORY";
+    case BSA_ERR_HIP: return "BSA_ERR_HIP";
+    case BSA_ERR_TABLE: return "BSA_ERR_TABLE";
+    default: return "BSA_ERR_UNKNOWN";
+  }
+}
+
+const char* bsa_last_error(void) { return g_err.c_str(); }
+
+int32_t bsa_catalog_size(void) { return (int32_t)catalog().size(); }
+
+bsa_status bsa_catalog_get(int32_t id, bsa_catalog_entry* out) {
+  if (!out || id < 0 || id >= (int)catalog().size()) return fail(BSA_ERR_INVALID_ARG, "bad catalog id %d", id);
+  const CatalogEntry& e = catalog()[id];
+  std::memset(out, 0, sizeof *out);
+  out->id = e.id;
+  out->tile_q = e.tq;
+  out->tile_kv = e.tkv;
+  out->d = e.d;
+  out->split = e.split;
+  out->xcd_remap = e.xcd_remap;
+  std::snprintf(out->name, sizeof out->name, "%s", e.name.c_str());
+  return BSA_OK;
+}
+
+const char* bsa_catalog_hash(void) {
+  static std::string s = [] {
+    char buf[32];
+    std::snprintf(buf, sizeof buf, "%016llx", (unsigned long long)catalog_hash_value());
+    return std::string(buf);
+  }();
+  return s.c_str();
+}
+
+const char* bsa_table_version(void) {
+  thread_local std::string v;
+  v = table_version();
+  return v.c_str();
+}
+
+bsa_status bsa_table_load(const char* path) {
+  std::string err;
+  bsa_status st = table_load_file(path, &err);
+  if (st != BSA_OK) return fail(st, "%s", err.c_str());
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_eligible(int32_t id, const bsa_request* req, int32_t* out) {
+  if (!req || !out || id < 0 || id >= (int)catalog().size())
+    return fail(BSA_ERR_INVALID_ARG, "bad arguments to bsa_plan_eligible");
+  std::string why;
+  *out = eligible(catalog()[id], *req, -1, &why) ? 1 : 0;
+  return BSA_OK;
+}
+
+bsa_status bsa_select(const bsa_request* req, double density, double run_coverage, int32_t* plan_id,
+                      int32_t* regime) {
+  if (!req || !plan_id || !regime) return fail(BSA_ERR_INVALID_ARG, "NULL argument to bsa_select");
+  Selection s = lookup(*req, density, run_coverage);
+  *regime = s.regime;
+  for (int c : s.candidates) {
+    if (eligible(catalog()[c], *req, -1, nullptr)) {
+      *plan_id = c;
+      return BSA_OK;
+    }
+  }
+  *plan_id = -1;
+  return fail(BSA_ERR_UNSUPPORTED, "no eligible plan for B=(%d,%d) d=%d", req->block_q, req->block_kv, req->d);
+}
+
+bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  bsa_status vs = validate_request(req);
+  if (vs != BSA_OK) return vs;
+  hipStream_t s = (hipStream_t)stream;
+  std::unique_ptr<bsa_plan> p(new bsa_plan());
+  p->req = *req;
+  p->req.mask = nullptr;  // not retained
+  HIP_TRY(hipGetDevice(&p->dev));
+  const bsa_request& r = *req;
+  p->nqb = (int)cdiv(r.N, r.block_q);
+  p->nkb = (int)cdiv(r.N, r.block_kv);
+  const int nrows = r.H * p->nqb;
+
+  // ---- shared mask state: counts, offsets, statistics -------------------------
+  HIP_TRY(pool_alloc(p->dev, sizeof(MaskStats), &p->stats_dev));
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nrows + 1), &p->row_ptr));
+  MaskStats* dst = (MaskStats*)p->stats_dev.ptr;
+  HIP_TRY(launch_zero_stats(dst, s));
+  HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, dst, s));
+  HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, &dst->nnz, s));
+  MaskStats* host = pinned_stats();
+  if (!host) return fail(BSA_ERR_NO_MEMORY, "pinned host allocation failed");
+  HIP_TRY(hipMemcpyAsync(host, dst, sizeof(MaskStats), hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  p->stats = *host;
+  const double total_blocks = (double)r.H * p->nqb * p->nkb;
+  const double density = p->stats.nnz / total_blocks;
+  const double runcov = p->stats.nnz ? (double)p->stats.long_run / (double)p->stats.nnz : 0.0;
+
+  // ---- regime lookup and ranked fallback ------------------------------------
+  const auto t0 = std::chrono::steady_clock::now();
+  Selection sel;
+  if (r.force_plan >= 0) {
+    sel.regime = -2;
+    sel.candidates = {r.force_plan};
+  } else {
+    sel = lookup(r, density, runcov);
+  }
+  const CatalogEntry* chosen = nullptr;
+  PlanShape shape;
+  std::string why = "no candidate";
+  for (int c : sel.candidates) {
+    const CatalogEntry& e = catalog()[c];
+    if (!attn_launcher(e.tq, e.tkv, e.d)) continue;
+    PlanShape sh = shape_plan(e, r, p->stats, p->dev);
+    if (eligible(e, r, sh.ws_bytes, &why)) {
+      chosen = &e;
+      shape = sh;
+      break;
+    }
+  }
+  const auto t1 = std::chrono::steady_clock::now();
+  if (!chosen)
+    return fail(BSA_ERR_UNSUPPORTED, "no eligible plan for B=(%d,%d) d=%d (%s)", r.block_q, r.block_kv, r.d,
+                why.c_str());
+  p->entry = chosen;
+  p->shape = shape;
+
+  // ---- block-CSR columns ------------------------------------------------------
+  const size_t nnz = (size_t)p->stats.nnz;
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->cols));
+  HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
+
+  // ---- launch preparation: tile list of the selected mapping -------------------
+  const int cq = shape.mq.coarsen, ckv = shape.mk.coarsen;
+  p->coarse = cq > 1 || ckv > 1;
+  if (p->coarse) {
+    p->ntr = (int)cdiv(p->nqb, cq);
+    const int ntc = (int)cdiv(p->nkb, ckv);
+    const int ntrows = r.H * p->ntr;
+    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)ntrows, &p->trow_cnt));
+    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)ntrows + 1), &p->trow_ptr_buf));
+    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->tcol_buf));
+    HIP_TRY(pool_alloc(p->dev, sizeof(uint32_t) * std::max<size_t>(nnz, 1), &p->tbits_buf));
+    HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
+                           ntc, (int32_t*)p->trow_cnt.ptr, nullptr, nullptr, nullptr, s));
+    HIP_TRY(launch_scan((int32_t*)p->trow_cnt.ptr, (int32_t*)p->trow_ptr_buf.ptr, ntrows, nullptr, s));
+    HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
+                           ntc, nullptr, (int32_t*)p->trow_ptr_buf.ptr, (int32_t*)p->tcol_buf.ptr,
+                           (uint32_t*)p->tbits_buf.ptr, s));
+    p->trow_ptr = (const int32_t*)p->trow_ptr_buf.ptr;
+    p->tcol = (const int32_t*)p->tcol_buf.ptr;
+    p->tbits = (const uint32_t*)p->tbits_buf.ptr;
+  } else {
+    p->ntr = p->nqb;
+    p->trow_ptr = (const int32_t*)p->row_ptr.ptr;
+    p->tcol = (const int32_t*)p->cols.ptr;
+    p->tbits = nullptr;
+  }
+
+  // ---- tasks and split-K partitions -----------------------------------------
+  const int64_t nqt = shape.nqt;
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->parts));
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->slots));
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nqt + 1), &p->task_off));
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nqt + 1), &p->slot_off));
+  HIP_TRY(pool_alloc(p->dev, sizeof(Task) * (size_t)std::max<int64_t>(shape.tasks_upper, 1), &p->tasks));
+  HIP_TRY(launch_task_count(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split,
+                            (int32_t*)p->parts.ptr, (int32_t*)p->slots.ptr, s));
+  HIP_TRY(launch_scan((int32_t*)p->parts.ptr, (int32_t*)p->task_off.ptr, (int32_t)nqt, &dst->n_tasks, s));
+  HIP_TRY(launch_scan((int32_t*)p->slots.ptr, (int32_t*)p->slot_off.ptr, (int32_t)nqt, nullptr, s));
+  HIP_TRY(launch_task_write(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, (int32_t*)p->parts.ptr,
+                            (int32_t*)p->task_off.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr, s));
+  if (shape.slots_upper > 0) HIP_TRY(pool_alloc(p->dev, (size_t)shape.ws_bytes, &p->ws));
+  p->grid = chosen->xcd_remap ? cdiv(shape.tasks_upper, 8) * 8 : shape.tasks_upper;
+  if (p->grid < 1) p->grid = chosen->xcd_remap ? 8 : 1;
+  if (p->grid >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many tasks");
+  HIP_TRY(hipGetLastError());
+
+  bsa_plan_info& in = p->info;
+  in.plan_id = chosen->id;
+  in.regime = sel.regime;
+  in.tile_q = chosen->tq;
+  in.tile_kv = chosen->tkv;
+  in.coarsen_q = cq;
+  in.coarsen_kv = ckv;
+  in.refine_q = shape.mq.refine;
+  in.refine_kv = shape.mk.refine;
+  in.split_items = shape.split;
+  in.max_row_nnz = (int32_t)p->stats.max_row_nnz;
+  in.nnz_blocks = (int64_t)p->stats.nnz;
+  in.n_tile_rows = (int64_t)r.H * p->ntr;
+  in.n_items = -1;  // known on the device; filled by export
+  in.n_tasks = -1;
+  in.grid = p->grid;
+  in.workspace_bytes = shape.slots_upper > 0 ? shape.ws_bytes : 0;
+  in.long_run_blocks = (int64_t)p->stats.long_run;
+  in.density = density;
+  in.run_coverage = runcov;
+  in.host_select_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+  *out = p.release();
+  return BSA_OK;
+}
+
+static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, const void* v, void* o,
+                           hipStream_t s, bool timed, float* attn_ms, float* merge_ms) {
+  if (!p) return fail(BSA_ERR_INVALID_ARG, "plan is NULL");
+  if (!q || !k || !v || !o) return fail(BSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  for (const void* ptr : {q, k, v, (const void*)o})
+    if (((uintptr_t)ptr) & 15) return fail(BSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const bsa_request& r = p->req;
+  const uintptr_t bytes = (uintptr_t)r.H * r.N * r.d * 2;
+  for (const void* in : {q, k, v}) {
+    const uintptr_t a = (uintptr_t)in, b = (uintptr_t)o;
+    if (a < b + bytes && b < a + bytes) return fail(BSA_ERR_INVALID_ARG, "O overlaps Q, K or V");
+  }
+  const CatalogEntry& e = *p->entry;
+  AttnLauncher fn = attn_launcher(e.tq, e.tkv, e.d);
+  if (!fn) return fail(BSA_ERR_UNSUPPORTED, "no kernel for plan %s", e.name.c_str());
+  AttnArgs a{};
+  a.q = (const __bf16*)q;
+  a.k = (const __bf16*)k;
+  a.v = (const __bf16*)v;
+  a.o = (__bf16*)o;
+  a.tasks = (const Task*)p->tasks.ptr;
+  a.n_tasks = &((const MaskStats*)p->stats_dev.ptr)->n_tasks;
+  a.tcol = p->tcol;
+  a.tbits = p->tbits;
+  float* ws = (float*)p->ws.ptr;
+  const int64_t slots = p->shape.slots_upper;
+  a.ws_m = ws;
+  a.ws_l = ws ? ws + slots * e.tq : nullptr;
+  a.ws_o = ws ? ws + 2 * slots * e.tq : nullptr;
+  a.N = r.N;
+  a.sub_log2 = ilog2(p->shape.mk.refine);
+  a.bkv_log2 = ilog2(r.block_kv);
+  a.coarsen_kv = p->shape.mk.coarsen;
+  a.coarsen_q = p->shape.mq.coarsen;
+  a.bq = r.block_q;
+  a.xcd_remap = e.xcd_remap;
+  a.grid = (int32_t)p->grid;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)r.d));
+  bsa_plan* mp = const_cast<bsa_plan*>(p);
+  if (timed) {
+    for (auto& ev : mp->ev)
+      if (!ev) HIP_TRY(hipEventCreate(&ev));
+    HIP_TRY(hipEventRecord(mp->ev[0], s));
+  }
+  HIP_TRY(fn(a, (int)p->grid, s));
+  if (timed) HIP_TRY(hipEventRecord(mp->ev[1], s));
+  if (p->shape.split > 0) {
+    MergeArgs m{};
+    m.o = (__bf16*)o;
+    m.parts = (const int32_t*)p->parts.ptr;
+    m.slot_base = (const int32_t*)p->slot_off.ptr;
+    m.ws_m = a.ws_m;
+    m.ws_l = a.ws_l;
+    m.ws_o = a.ws_o;
+    m.N = r.N;
+    m.n_qtiles_head = p->shape.nqt_head;
+    m.tq = e.tq;
+    m.d = e.d;
+    HIP_TRY(launch_merge(m, (int32_t)p->shape.nqt, s));
+  }
+  if (timed) {
+    HIP_TRY(hipEventRecord(mp->ev[2], s));
+    HIP_TRY(hipEventSynchronize(mp->ev[2]));
+    float t = 0;
+    HIP_TRY(hipEventElapsedTime(&t, mp->ev[0], mp->ev[1]));
+    if (attn_ms) *attn_ms = t;
+    HIP_TRY(hipEventElapsedTime(&t, mp->ev[1], mp->ev[2]));
+    if (merge_ms) *merge_ms = t;
+  }
+  return BSA_OK;
+}
+
+bsa_status bsa_run(const bsa_plan* p, const void* q, const void* k, const void* v, void* o, void* stream) {
+  return run_impl(p, q, k, v, o, (hipStream_t)stream, false, nullptr, nullptr);
+}
+
+bsa_status bsa_run_timed(const bsa_plan* p, const void* q, const void* k, const void* v, void* o, void* stream,
+                         float* attn_ms, float* merge_ms) {
+  return run_impl(p, q, k, v, o, (hipStream_t)stream, true, attn_ms, merge_ms);
+}
+
+bsa_status bsa_plan_destroy(bsa_plan* p) {
+  if (!p) return BSA_OK;
+  hipError_t e = hipDeviceSynchronize();
+  delete p;
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_get_info(const bsa_plan* p, bsa_plan_info* info) {
+  if (!p || !info) return fail(BSA_ERR_INVALID_ARG, "NULL argument");
+  *info = p->info;
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_export_csr(const bsa_plan* p, int32_t* row_ptr, int32_t* cols, int64_t cap_cols) {
+  if (!p || !row_ptr || !cols) return fail(BSA_ERR_INVALID_ARG, "NULL argument");
+  if (cap_cols < (int64_t)p->stats.nnz) return fail(BSA_ERR_INVALID_ARG, "cols capacity too small");
+  const size_t nrows = (size_t)p->req.H * p->nqb;
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(row_ptr, p->row_ptr.ptr, sizeof(int32_t) * (nrows + 1), hipMemcpyDeviceToHost));
+  if (p->stats.nnz)
+    HIP_TRY(hipMemcpy(cols, p->cols.ptr, sizeof(int32_t) * (size_t)p->stats.nnz, hipMemcpyDeviceToHost));
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_export_tiles(const bsa_plan* p, int32_t* head, int32_t* q_tile, int32_t* kv_tile,
+                                 uint32_t* bits, int64_t cap, int64_t* count) {
+  if (!p || !count) return fail(BSA_ERR_INVALID_ARG, "NULL argument");
+  HIP_TRY(hipDeviceSynchronize());
+  MaskStats st{};
+  HIP_TRY(hipMemcpy(&st, p->stats_dev.ptr, sizeof st, hipMemcpyDeviceToHost));
+  const size_t nt = (size_t)st.n_tasks;
+  std::vector<Task> tasks(nt);
+  if (nt) HIP_TRY(hipMemcpy(tasks.data(), p->tasks.ptr, sizeof(Task) * nt, hipMemcpyDeviceToHost));
+  const size_t ntrows = (size_t)p->req.H * p->ntr;
+  int32_t nitems = 0;
+  HIP_TRY(hipMemcpy(&nitems, p->trow_ptr + ntrows, sizeof(int32_t), hipMemcpyDeviceToHost));
+  std::vector<int32_t> tcol(nitems);
+  std::vector<uint32_t> tbits;
+  if (nitems) HIP_TRY(hipMemcpy(tcol.data(), p->tcol, sizeof(int32_t) * nitems, hipMemcpyDeviceToHost));
+  if (p->tbits) {
+    tbits.resize(nitems);
+    if (nitems) HIP_TRY(hipMemcpy(tbits.data(), p->tbits, sizeof(uint32_t) * nitems, hipMemcpyDeviceToHost));
+  }
+  const int rkv = p->shape.mk.refine;
+  const int tkv = p->entry->tkv;
+  const int N = p->req.N;
+  const uint32_t full = (p->shape.mq.coarsen * p->shape.mk.coarsen >= 32)
+                            ? 0xffffffffu
+                            : ((1u << (p->shape.mq.coarsen * p->shape.mk.coarsen)) - 1u);
+  int64_t n = 0;
+  for (const Task& t : tasks) {
+    for (int it = t.begin; it < t.end; ++it) {
+      for (int sub = 0; sub < rkv; ++sub) {
+        const int kt = tcol[it] * rkv + sub;
+        if ((int64_t)kt * tkv >= N) continue;
+        if (n < cap && head && q_tile && kv_tile && bits) {
+          head[n] = t.head;
+          q_tile[n] = t.qtile;
+          kv_tile[n] = kt;
+          bits[n] = p->tbits ? tbits[it] : full;
+        }
+        ++n;
+      }
+    }
+  }
+  *count = n;
+  const_cast<bsa_plan*>(p)->info.n_items = nitems;
+  const_cast<bsa_plan*>(p)->info.n_tasks = (int64_t)nt;
+  if (n > cap) return fail(BSA_ERR_INVALID_ARG, "capacity %lld < %lld tiles", (long long)cap, (long long)n);
+  return BSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Instantiations of the attention mainloop (the native kernel catalog's
+// kernels, one per physical tile shape and head dimension).
+#include "attn_fwd.h"
+
+namespace bsa {
+
+AttnLauncher attn_launcher(int tq, int tkv, int d) {
+#define BSA_CASE(TQ_, TKV_, D_) \
+  if (tq == TQ_ && tkv == TKV_ && d == D_) return &launch_attn<TQ_, TKV_, D_>;
+  BSA_CASE(64, 32, 128)
+  BSA_CASE(64, 64, 128)
+  BSA_CASE(128, 32, 128)
+  BSA_CASE(128, 64, 128)
+  BSA_CASE(128, 128, 128)
+  BSA_CASE(64, 32, 64)
+  BSA_CASE(64, 64, 64)
+  BSA_CASE(128, 32, 64)
+  BSA_CASE(128, 64, 64)
+  BSA_CASE(128, 128, 64)
+#undef BSA_CASE
+  return nullptr;
+}
+
+int attn_wg_per_cu(int tq, int tkv, int d) {
+  int n = 0;
+#define BSA_CASE(TQ_, TKV_, D_)                                                               \
+  if (tq == TQ_ && tkv == TKV_ && d == D_) {                                                  \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel<TQ_, TKV_, D_>,      \
+                                                     TQ_ * 2, 0) != hipSuccess)               \
+      n = 0;                                                                                  \
+    return n;                                                                                 \
+  }
+  BSA_CASE(64, 32, 128)
+  BSA_CASE(64, 64, 128)
+  BSA_CASE(128, 32, 128)
+  BSA_CASE(128, 64, 128)
+  BSA_CASE(128, 128, 128)
+  BSA_CASE(64, 32, 64)
+  BSA_CASE(64, 64, 64)
+  BSA_CASE(128, 32, 64)
+  BSA_CASE(128, 64, 64)
+  BSA_CASE(128, 128, 64)
+#undef BSA_CASE
+  return 0;
+}
+
+}  // namespace bsa

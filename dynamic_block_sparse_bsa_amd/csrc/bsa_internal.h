@@ -1,0 +1,98 @@
+// Internal declarations shared by the host code and the gfx950 kernels of the
+// block-sparse attention library.  Nothing here is part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// One workgroup task of the attention launch: a query tile of one head and a
+// contiguous range [begin, end) of entries of the tile list (the block-CSR for
+// Direct and Refined mappings, the coarsened tile list otherwise).  slot >= 0
+// marks a split-K partition whose partial state goes to workspace slot `slot`.
+struct Task {
+  int32_t head;
+  int32_t qtile;
+  int32_t begin;
+  int32_t end;
+  int32_t slot;
+  int32_t pad0, pad1, pad2;
+};
+static_assert(sizeof(Task) == 32, "Task is 32 bytes");
+
+// Statistics of the shared mask state, filled on the GPU and copied to the
+// host in one transfer.
+struct MaskStats {
+  unsigned long long nnz;            // active logical blocks
+  unsigned long long long_run;       // active blocks inside runs of length >= 2
+  unsigned int max_row_nnz;          // largest active count of a query-block row
+  unsigned int empty_rows;           // query-block rows with no active block
+  unsigned long long n_tasks;        // tasks written by the task builder
+};
+
+// Arguments of the attention mainloop kernels.
+struct AttnArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  const Task* tasks;
+  const unsigned long long* n_tasks;  // device count written by the task builder
+  const int32_t* tcol;    // tile-list column (in units of the list's column width)
+  const uint32_t* tbits;  // membership bits per tile-list entry, or nullptr
+  float* ws_m;            // [slot][T_Q]           running max (log2 units)
+  float* ws_l;            // [slot][T_Q]           exponential sum
+  float* ws_o;            // [slot][d][T_Q]        unnormalized accumulator
+  int32_t N;
+  int32_t sub_log2;       // log2(refine_kv): K/V tiles per tile-list entry
+  int32_t bkv_log2;       // log2(B_KV)
+  int32_t coarsen_kv;     // logical K/V blocks per tile (membership decode)
+  int32_t bq;             // B_Q (membership decode when coarsen_q > 1)
+  int32_t coarsen_q;
+  int32_t xcd_remap;      // 1: group consecutive tasks on one XCD
+  int32_t grid;           // workgroups launched (multiple of 8 when remapped)
+  float scale_log2;       // log2(e) / sqrt(d)
+};
+
+struct MergeArgs {
+  __bf16* o;
+  const int32_t* parts;     // [n_qtiles] partitions per query tile
+  const int32_t* slot_base; // [n_qtiles] first workspace slot of the query tile
+  const float* ws_m;
+  const float* ws_l;
+  const float* ws_o;
+  int32_t N;
+  int32_t n_qtiles_head;    // query tiles per head
+  int32_t tq;
+  int32_t d;
+};
+
+// Kernel launchers (defined in the .hip translation units).
+using AttnLauncher = hipError_t (*)(const AttnArgs&, int grid, hipStream_t);
+
+hipError_t launch_zero_stats(MaskStats* st, hipStream_t s);
+hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_cnt,
+                            MaskStats* st, hipStream_t s);
+hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, unsigned long long* total,
+                       hipStream_t s);
+hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
+                          int32_t* cols, hipStream_t s);
+hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,
+                          int32_t nkb, int32_t cq, int32_t ckv, int32_t ntr, int32_t ntc,
+                          int32_t* trow_cnt, const int32_t* trow_ptr, int32_t* tcol,
+                          uint32_t* tbits, hipStream_t s);
+hipError_t launch_task_count(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
+                             int32_t refine_q, int32_t split, int32_t* parts, int32_t* slots,
+                             hipStream_t s);
+hipError_t launch_task_write(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
+                             int32_t refine_q, const int32_t* parts, const int32_t* task_off,
+                             const int32_t* slot_off, Task* tasks, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s);
+
+// Attention kernel table: returns nullptr when (tq, tkv, d) has no kernel.
+AttnLauncher attn_launcher(int tq, int tkv, int d);
+// Resident workgroups per CU of that kernel (0 if it has none).
+int attn_wg_per_cu(int tq, int tkv, int d);
+
+}  // namespace bsa

@@ -1,0 +1,313 @@
+// Catalog, eligibility, and the versioned plan table (host only; no GPU calls).
+#include "catalog.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <fstream>
+#include <mutex>
+#include <sstream>
+
+namespace bsa {
+
+namespace {
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+std::vector<CatalogEntry> build_catalog() {
+  // kernel tile shapes instantiated for gfx950 (see attn_kernels.hip)
+  static const int shapes[][2] = {{64, 32}, {64, 64}, {128, 32}, {128, 64}, {128, 128}};
+  std::vector<CatalogEntry> c;
+  for (int d : {128, 64}) {
+    for (auto& s : shapes) {
+      // organizations: no split; split-K balance rule; split-K + per-XCD grouping
+      const int orgs[][2] = {{1, 0}, {0, 0}, {1, 1}};
+      for (auto& o : orgs) {
+        CatalogEntry e;
+        e.id = (int)c.size();
+        e.tq = s[0];
+        e.tkv = s[1];
+        e.d = d;
+        e.split = o[0];
+        e.xcd_remap = o[1];
+        char buf[48];
+        std::snprintf(buf, sizeof buf, "T%dx%d_d%d_%s%s", e.tq, e.tkv, d, e.split ? "splitk" : "nosplit",
+                      e.xcd_remap ? "_xcd" : "");
+        e.name = buf;
+        c.push_back(e);
+      }
+    }
+  }
+  return c;
+}
+
+struct Bounds {
+  std::vector<double> H, N, density, runcov;
+};
+
+struct Regime {
+  int bq, bkv, d;
+  int hb, nb, db, rb;  // bucket index per feature, -1 = any
+  std::vector<int> ranking;
+};
+
+struct Table {
+  std::string version = "builtin-empty";
+  Bounds bounds;
+  std::vector<Regime> regimes;
+};
+
+std::mutex g_table_mu;
+Table g_table;
+bool g_table_init = false;
+
+int bucket(const std::vector<double>& b, double x) {
+  int k = 0;
+  while (k < (int)b.size() && x >= b[k]) ++k;
+  return k;
+}
+
+const char* builtin_table_text();
+bsa_status parse_table(const std::string& text, Table* out, std::string* err);
+
+// Called with g_table_mu held: install the built-in artifact on first use.
+void ensure_table() {
+  if (g_table_init) return;
+  g_table_init = true;
+  Table t;
+  std::string err;
+  if (parse_table(builtin_table_text(), &t, &err) == BSA_OK) g_table = t;
+}
+
+}  // namespace
+
+DimMap map_dim(int block, int tile, int min_coarsen_block) {
+  DimMap m;
+  if (block <= 0 || tile <= 0 || !pow2(block) || !pow2(tile)) return m;
+  if (tile == block) {
+    m.ok = true;
+  } else if (tile > block) {
+    if (block < min_coarsen_block) return m;
+    m.ok = true;
+    m.coarsen = tile / block;
+  } else {
+    m.ok = true;
+    m.refine = block / tile;
+  }
+  return m;
+}
+
+const std::vector<CatalogEntry>& catalog() {
+  static const std::vector<CatalogEntry> c = build_catalog();
+  return c;
+}
+
+uint64_t catalog_hash_value() {
+  uint64_t h = 1469598103934665603ull;  // FNV-1a over the entry names
+  for (auto& e : catalog()) {
+    for (char ch : e.name) {
+      h ^= (unsigned char)ch;
+      h *= 1099511628211ull;
+    }
+    h ^= 0xff;
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+bool eligible(const CatalogEntry& e, const bsa_request& r, int64_t ws_bytes, std::string* why) {
+  auto no = [&](const char* s) {
+    if (why) *why = s;
+    return false;
+  };
+  if (r.dtype != BSA_DTYPE_BF16) return no("dtype");
+  if (r.layout != BSA_LAYOUT_HND) return no("layout");
+  if (r.d != e.d) return no("head dim");
+  // a wave owns 32 query rows, so a coarsened query tile needs B_Q >= 32
+  DimMap mq = map_dim(r.block_q, e.tq, 32);
+  DimMap mk = map_dim(r.block_kv, e.tkv, 1);
+  if (!mq.ok) return no("query geometry");
+  if (!mk.ok) return no("key/value geometry");
+  if (mq.coarsen * mk.coarsen > 32) return no("membership bits");
+  if (ws_bytes >= 0 && r.workspace_limit > 0 && ws_bytes > r.workspace_limit) return no("workspace");
+  return true;
+}
+
+int base_plan(const bsa_request& r) {
+  const auto& c = catalog();
+  for (auto& e : c)
+    if (e.tq == r.block_q && e.tkv == r.block_kv && e.d == r.d && e.split == 1 && e.xcd_remap == 0 &&
+        eligible(e, r, -1, nullptr))
+      return e.id;
+  int best = -1;
+  for (auto& e : c) {
+    if (e.split != 1 || e.xcd_remap != 0 || !eligible(e, r, -1, nullptr)) continue;
+    if (best < 0 || e.tq * e.tkv < c[best].tq * c[best].tkv) best = e.id;
+  }
+  return best;
+}
+
+Selection lookup(const bsa_request& r, double density, double run_coverage) {
+  std::lock_guard<std::mutex> lk(g_table_mu);
+  ensure_table();
+  Selection s;
+  const Table& t = g_table;
+  const int hb = bucket(t.bounds.H, r.H), nb = bucket(t.bounds.N, r.N);
+  const int db = bucket(t.bounds.density, density), rb = bucket(t.bounds.runcov, run_coverage);
+  for (size_t i = 0; i < t.regimes.size(); ++i) {
+    const Regime& g = t.regimes[i];
+    if (g.bq != r.block_q || g.bkv != r.block_kv || g.d != r.d) continue;
+    if ((g.hb >= 0 && g.hb != hb) || (g.nb >= 0 && g.nb != nb) || (g.db >= 0 && g.db != db) ||
+        (g.rb >= 0 && g.rb != rb))
+      continue;
+    s.regime = (int)i;
+    s.candidates = g.ranking;
+    break;
+  }
+  const int base = base_plan(r);
+  if (base >= 0 && std::find(s.candidates.begin(), s.candidates.end(), base) == s.candidates.end())
+    s.candidates.push_back(base);
+  return s;
+}
+
+// ---- table text format ------------------------------------------------------
+//   bsa-plan-table <version>
+//   arch gfx950
+//   catalog <hex hash of the catalog>
+//   bounds <H|N|density|run_coverage> v1 v2 ...     (bucket k: b[k-1] <= x < b[k])
+//   regime <B_Q> <B_KV> <d> <hb> <nb> <db> <rb> : <plan name> <plan name> ...
+// Lines starting with '#' are comments; '*' matches any bucket.
+namespace {
+bsa_status parse_table(const std::string& text, Table* out, std::string* err) {
+  Table t;
+  std::istringstream is(text);
+  std::string line;
+  bool have_header = false, have_arch = false, have_cat = false;
+  int lineno = 0;
+  auto fail = [&](const std::string& m) {
+    if (err) *err = "plan table line " + std::to_string(lineno) + ": " + m;
+    return BSA_ERR_TABLE;
+  };
+  std::vector<std::string> names;
+  for (auto& e : catalog()) names.push_back(e.name);
+  while (std::getline(is, line)) {
+    ++lineno;
+    if (line.empty() || line[0] == '#') continue;
+    std::istringstream ls(line);
+    std::string kw;
+    ls >> kw;
+    if (kw.empty()) continue;
+    if (kw == "bsa-plan-table") {
+      ls >> t.version;
+      if (t.version.empty()) return fail("missing version");
+      have_header = true;
+    } else if (kw == "arch") {
+      std::string a;
+      ls >> a;
+      if (a != "gfx950") return fail("table built for architecture " + a);
+      have_arch = true;
+    } else if (kw == "catalog") {
+      std::string h;
+      ls >> h;
+      char buf[32];
+      std::snprintf(buf, sizeof buf, "%016llx", (unsigned long long)catalog_hash_value());
+      if (h != buf) return fail("catalog hash " + h + " does not match " + buf);
+      have_cat = true;
+    } else if (kw == "bounds") {
+      std::string f;
+      ls >> f;
+      std::vector<double> v;
+      double x;
+      while (ls >> x) v.push_back(x);
+      if (!std::is_sorted(v.begin(), v.end())) return fail("bounds not sorted");
+      if (f == "H") t.bounds.H = v;
+      else if (f == "N") t.bounds.N = v;
+      else if (f == "density") t.bounds.density = v;
+      else if (f == "run_coverage") t.bounds.runcov = v;
+      else return fail("unknown feature " + f);
+    } else if (kw == "regime") {
+      Regime g;
+      std::string tok[7];
+      for (auto& s : tok) ls >> s;
+      auto num = [&](const std::string& s, int* out) {
+        if (s == "*") {
+          *out = -1;
+          return true;
+        }
+        char* end = nullptr;
+        long v = std::strtol(s.c_str(), &end, 10);
+        if (s.empty() || *end) return false;
+        *out = (int)v;
+        return true;
+      };
+      int* outs[7] = {&g.bq, &g.bkv, &g.d, &g.hb, &g.nb, &g.db, &g.rb};
+      for (int i = 0; i < 7; ++i)
+        if (!num(tok[i], outs[i])) return fail("bad regime field '" + tok[i] + "'");
+      std::string colon;
+      ls >> colon;
+      if (colon != ":") return fail("expected ':'");
+      std::string nm;
+      while (ls >> nm) {
+        auto it = std::find(names.begin(), names.end(), nm);
+        if (it == names.end()) return fail("unknown plan " + nm);
+        g.ranking.push_back((int)(it - names.begin()));
+      }
+      if (g.ranking.empty()) return fail("empty ranking");
+      t.regimes.push_back(g);
+    } else {
+      return fail("unknown keyword " + kw);
+    }
+  }
+  if (!have_header || !have_arch || !have_cat) {
+    lineno = 0;
+    return fail("missing header, arch or catalog line");
+  }
+  *out = t;
+  return BSA_OK;
+}
+}  // namespace
+
+bsa_status table_load_text(const std::string& text, std::string* err) {
+  Table t;
+  bsa_status st = parse_table(text, &t, err);
+  if (st != BSA_OK) return st;
+  std::lock_guard<std::mutex> lk(g_table_mu);
+  g_table = t;
+  g_table_init = true;
+  return BSA_OK;
+}
+
+bsa_status table_load_file(const char* path, std::string* err) {
+  if (!path) {
+    std::lock_guard<std::mutex> lk(g_table_mu);
+    g_table_init = false;
+    g_table = Table();
+    ensure_table();
+    return BSA_OK;
+  }
+  std::ifstream f(path);
+  if (!f) {
+    if (err) *err = std::string("cannot open plan table ") + path;
+    return BSA_ERR_TABLE;
+  }
+  std::stringstream ss;
+  ss << f.rdbuf();
+  return table_load_text(ss.str(), err);
+}
+
+const std::string& table_version() {
+  std::lock_guard<std::mutex> lk(g_table_mu);
+  ensure_table();
+  return g_table.version;
+}
+
+namespace {
+const char* builtin_table_text() {
+  return
+#include "table_builtin.inc"
+      ;
+}
+}  // namespace
+
+}  // namespace bsa

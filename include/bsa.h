@@ -1,0 +1,185 @@
+/*
+ * bsa.h -- C ABI of the MI355X (gfx950) block-sparse attention library.
+ *
+ * Forward pass of dynamic block-sparse attention (BSA) as described in
+ * "Decoupling Logical Masks from GPU Execution for Dynamic Block-Sparse
+ * Attention" (Tessera):
+ *   - a request carries a logical block mask M over block geometry
+ *     B = (B_Q, B_KV), tensor properties (dtype, head dim, layout) and the
+ *     request dimensions (heads, sequence length)      [paper section 3,
+ *     "Online request path"; section 4.4 request R = <A, M, B, x>]
+ *   - plan creation builds the shared mask state (block-CSR plus scalar
+ *     statistics) on the GPU, copies only the statistics to the host, looks
+ *     up the performance regime, scans its ranking for the first eligible
+ *     plan and prepares only that plan's metadata     [section 5.2]
+ *   - run executes the plan's kernels: the attention mainloop and, for
+ *     split-K plans, the partial-state merge          [sections 4.2, 4.3]
+ *
+ * Semantics of the output (section 1, section 2.2): for each head h and
+ * query i < N, the keys j < N whose logical block M[h][i/B_Q][j/B_KV] is
+ * nonzero enter softmax(q_i k_j^T / sqrt(d)) v_j; a query row with no active
+ * key outputs zeros.  Non-causal.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device pointers; "host" pointers are
+ *     ordinary CPU memory.  The caller owns every buffer it passes in.
+ *   - Streams are hipStream_t values passed as void* (NULL = null stream).
+ *   - Every call returns a bsa_status; no C++ exception crosses the ABI.
+ *     Arguments are validated before anything is launched, so an error
+ *     status leaves outputs untouched.  bsa_last_error() gives the text of
+ *     the most recent error on the calling thread.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1, /* malformed request, bad pointer or size        */
+  BSA_ERR_UNSUPPORTED = 2, /* no eligible plan (dtype, d, geometry, limits)  */
+  BSA_ERR_NO_MEMORY = 3,   /* device or host allocation failed               */
+  BSA_ERR_HIP = 4,         /* a HIP runtime call failed                      */
+  BSA_ERR_TABLE = 5        /* plan table missing, corrupt or mismatched      */
+} bsa_status;
+
+enum { BSA_DTYPE_BF16 = 1 };
+enum { BSA_LAYOUT_HND = 0 }; /* [H][N][d], d contiguous, no padding */
+
+/* Opaque prepared plan: owns the block-CSR, the selected plan's metadata
+ * (tile lists, membership bits, tasks) and its split-K workspace. */
+typedef struct bsa_plan bsa_plan;
+
+/* A runtime request (paper section 4.4: R = <A, M, B, x>; section 3 and
+ * section 5.1: batch, head count and sequence length).  Batch is folded into
+ * H. */
+typedef struct {
+  int32_t H;         /* heads (times batch), >= 1                               */
+  int32_t N;         /* sequence length (queries = keys), >= 1                  */
+  int32_t d;         /* head dimension: 64 or 128                               */
+  int32_t block_q;   /* B_Q: 32, 64, 128 or 256                                 */
+  int32_t block_kv;  /* B_KV: 16, 32, 64, 128 or 256                            */
+  int32_t dtype;     /* BSA_DTYPE_BF16                                          */
+  int32_t layout;    /* BSA_LAYOUT_HND                                          */
+  int32_t force_plan;  /* -1: regime table selection; >= 0: that catalog entry
+                          (must be eligible, else BSA_ERR_UNSUPPORTED)          */
+  int32_t force_split; /* -1: the plan's own split rule; 0: never split;
+                          k > 0: at most k K/V items per task                   */
+  int32_t reserved;
+  int64_t workspace_limit; /* bytes of split-K workspace allowed; 0 = no limit */
+  /* device, uint8 [H][ceil(N/B_Q)][ceil(N/B_KV)], nonzero = active.  Read
+   * only during bsa_plan_create (which synchronizes the stream once before
+   * returning); the caller may reuse it afterwards. */
+  const uint8_t* mask;
+} bsa_request;
+
+/* Scalar facts about a prepared plan (host copy). */
+typedef struct {
+  int32_t plan_id;      /* catalog index of the selected plan                   */
+  int32_t regime;       /* regime index in the plan table; -1 = lookup miss     */
+  int32_t tile_q, tile_kv;       /* physical tile T = (T_Q, T_KV)                */
+  int32_t coarsen_q, coarsen_kv; /* logical blocks per tile (1 if not coarsened)*/
+  int32_t refine_q, refine_kv;   /* tiles per logical block (1 if not refined)  */
+  int32_t split_items;  /* max K/V items per task; 0 = no split                 */
+  int32_t max_row_nnz;  /* largest active-block count of a query-block row      */
+  int64_t nnz_blocks;   /* active logical blocks                                */
+  int64_t n_tile_rows;  /* rows of the tile list (query tiles or tile rows)     */
+  int64_t n_items;      /* entries of the tile list                             */
+  int64_t n_tasks;      /* workgroup tasks of the attention launch              */
+  int64_t grid;         /* workgroups launched (>= n_tasks)                     */
+  int64_t workspace_bytes; /* split-K workspace bound to the plan               */
+  int64_t long_run_blocks; /* active blocks inside runs of length >= 2          */
+  double density;       /* active / all logical blocks (section 5.1)            */
+  double run_coverage;  /* long_run_blocks / active, 0 for an empty mask        */
+  double host_select_us;   /* host time spent in regime lookup + ranking scan   */
+} bsa_plan_info;
+
+/* Description of one catalog entry (paper section 4.4: native catalog). */
+typedef struct {
+  int32_t id;
+  int32_t tile_q, tile_kv, d;
+  int32_t split;        /* 0 = never split, 1 = balance rule                    */
+  int32_t xcd_remap;    /* 1 = tasks grouped per XCD                             */
+  char name[48];
+} bsa_catalog_entry;
+
+/* Create a plan for a request.  Builds the mask state on `stream`, copies the
+ * statistics to the host (the single synchronization of the request path),
+ * selects the plan and prepares its metadata on `stream`.  On BSA_OK, *out
+ * owns device memory until bsa_plan_destroy.  Errors: BSA_ERR_INVALID_ARG
+ * (null pointers, non-positive sizes), BSA_ERR_UNSUPPORTED (dtype, layout,
+ * d, geometry or forced plan not eligible), BSA_ERR_NO_MEMORY, BSA_ERR_HIP. */
+bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out);
+
+/* Run a prepared plan: O = BSA(Q, K, V).  Q, K, V, O are device bf16
+ * [H][N][d] buffers (layout BSA_LAYOUT_HND); O is fully written (zeros for
+ * empty rows).  Stream-ordered and asynchronous.  One run per plan may be in
+ * flight at a time (the split-K workspace is per plan).  Q/K/V may alias each
+ * other; O must not alias Q, K or V. */
+bsa_status bsa_run(const bsa_plan* plan, const void* q, const void* k, const void* v, void* o,
+                   void* stream);
+
+/* Same as bsa_run, and also returns the attention kernel's own duration in
+ * milliseconds, measured with HIP events recorded on `stream` around that
+ * launch (the call synchronizes on the end event). */
+bsa_status bsa_run_timed(const bsa_plan* plan, const void* q, const void* k, const void* v,
+                         void* o, void* stream, float* attn_ms, float* merge_ms);
+
+/* Release a plan (synchronizes the device first).  NULL is accepted. */
+bsa_status bsa_plan_destroy(bsa_plan* plan);
+
+/* Copy the plan's scalar facts to *info (host). */
+bsa_status bsa_plan_get_info(const bsa_plan* plan, bsa_plan_info* info);
+
+/* Export the physical tiles the attention kernels will visit, in task order,
+ * to host arrays of capacity `cap` records: head, query-tile index, K/V tile
+ * index (in units of T_Q and T_KV tokens) and the membership bits of the
+ * tile (bit a*coarsen_kv + b set = logical block (a, b) inside the tile is
+ * active; all bits of the tile's coarsen_q*coarsen_kv set when not
+ * coarsened).  *count receives the number of records; BSA_ERR_INVALID_ARG if
+ * cap is too small (count still set).  For coverage checks only. */
+bsa_status bsa_plan_export_tiles(const bsa_plan* plan, int32_t* head, int32_t* q_tile,
+                                 int32_t* kv_tile, uint32_t* bits, int64_t cap, int64_t* count);
+
+/* Copy the shared block-CSR (row offsets [H*ceil(N/B_Q)+1] and column
+ * indices [nnz_blocks]) to host arrays. */
+bsa_status bsa_plan_export_csr(const bsa_plan* plan, int32_t* row_ptr, int32_t* cols,
+                               int64_t cap_cols);
+
+/* Catalog introspection. */
+int32_t bsa_catalog_size(void);
+bsa_status bsa_catalog_get(int32_t id, bsa_catalog_entry* out);
+
+/* Eligibility predicate Eligible(P, R) for catalog entry `id` and the
+ * request's geometry and tensor properties (section 4.4); host only, touches
+ * no GPU.  *eligible receives 1 or 0. */
+bsa_status bsa_plan_eligible(int32_t id, const bsa_request* req, int32_t* eligible);
+
+/* Regime lookup and ranked fallback (section 5.2) on host-side features:
+ * returns the selected catalog id, the regime index (-1 on a lookup miss, in
+ * which case the key's base plan is the sole candidate) and BSA_OK, or
+ * BSA_ERR_UNSUPPORTED when no candidate is eligible.  Touches no GPU. */
+bsa_status bsa_select(const bsa_request* req, double density, double run_coverage,
+                      int32_t* plan_id, int32_t* regime);
+
+/* Load a versioned plan table (text artifact) replacing the built-in one.
+ * BSA_ERR_TABLE if unreadable, malformed, or built for another architecture
+ * or catalog.  NULL restores the built-in table. */
+bsa_status bsa_table_load(const char* path);
+
+/* Version strings of the loaded table and of the catalog. */
+const char* bsa_table_version(void);
+const char* bsa_catalog_hash(void);
+
+const char* bsa_status_string(int32_t status);
+const char* bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

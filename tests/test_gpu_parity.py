@@ -1,0 +1,97 @@
+"""GPU parity: the library (through the C ABI) against the fp64 oracle.
+
+Tolerance: max |err| <= 1e-2 and mean |err| <= 1e-3 on bf16-rounded inputs.
+Outputs are pre-filled with NaN so a row the kernels never write fails.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_bsa_amd as bsa
+from oracle import attention as oatt
+from oracle import coverage
+from workloads import gen
+
+from bsa_testutil import assert_close, gpu_run, tile_cells
+
+pytestmark = pytest.mark.gpu
+
+
+def _eligible_plans(H, N, d, block):
+    return [e["id"] for e in bsa.catalog() if bsa.eligible(e["id"], H, N, d, block)]
+
+
+@pytest.fixture(scope="module")
+def c1():
+    cfg = gen.config(1)
+    ref = oatt.attention(cfg["q"], cfg["k"], cfg["v"], cfg["mask"], 64, 64)
+    return cfg, ref
+
+
+def test_c1_every_eligible_plan(c1):
+    cfg, ref = c1
+    plans = _eligible_plans(1, 1024, 64, (64, 64))
+    assert len(plans) >= 6
+    for pid in plans:
+        for fs in (-1, 0, 2):
+            p, out = gpu_run(cfg["mask"], cfg["q"], cfg["k"], cfg["v"], (64, 64), force_plan=pid,
+                             force_split=fs)
+            assert_close(out, ref, f"plan {pid} split {fs}")
+            cov, cq, ckv = tile_cells(p, (64, 64), 1024)
+            assert (cov == coverage.cells(cfg["mask"], 64, 64, 1024, cq, ckv)).all()
+            p.destroy()
+
+
+GEOMS = [(64, 64), (128, 128), (128, 32), (32, 128), (64, 32), (32, 64)]
+
+
+@pytest.mark.parametrize("block", GEOMS)
+@pytest.mark.parametrize("N", [777, 1024])
+def test_small_all_plans(block, N):
+    H, d = 3, 128
+    seed = 100 + block[0] + 7 * block[1] + N
+    M, q, k, v = gen.random_case(H, N, d, *block, p=0.3, seed=seed,
+                                 empty_rows={1: [0, 2]}, dense_heads=(2,))
+    ref = oatt.attention(q, k, v, M, *block)
+    plans = _eligible_plans(H, N, d, block)
+    assert plans
+    for pid in plans:
+        for fs in (-1, 1):
+            p, out = gpu_run(M, q, k, v, block, force_plan=pid, force_split=fs)
+            assert_close(out, ref, f"B={block} N={N} plan {pid} split {fs}")
+            cov, cq, ckv = tile_cells(p, block, N)
+            assert (cov == coverage.cells(M, *block, N, cq, ckv)).all(), f"coverage plan {pid}"
+            p.destroy()
+
+
+def test_edge_cases():
+    d = 128
+    # empty mask: all zeros, no NaN
+    for N, block in ((300, (64, 64)), (20, (128, 32)), (1, (64, 64))):
+        nq, nk = -(-N // block[0]), -(-N // block[1])
+        q, k, v = gen.qkv(2, N, d, (1, 2, 3))
+        M = np.zeros((2, nq, nk), np.uint8)
+        p, out = gpu_run(M, q, k, v, block)
+        assert (out.float() == 0).all()
+        M[:] = 1
+        ref = oatt.attention(q, k, v, M, *block)
+        p, out = gpu_run(M, q, k, v, block)
+        assert_close(out, ref, f"dense N={N}")
+
+
+def test_determinism():
+    M, q, k, v = gen.random_case(4, 2000, 128, 64, 64, p=0.4, seed=9)
+    a = gpu_run(M, q, k, v, (64, 64), force_split=2)[1]
+    b = gpu_run(M, q, k, v, (64, 64), force_split=2)[1]
+    assert torch.equal(a, b)
+
+
+def test_c2_medium():
+    cfg = gen.config(2)
+    ref = oatt.attention(cfg["q"], cfg["k"], cfg["v"], cfg["mask"], 128, 128)
+    for pid in (-1,) + tuple(_eligible_plans(8, 8192, 128, (128, 128)))[:4]:
+        p, out = gpu_run(cfg["mask"], cfg["q"], cfg["k"], cfg["v"], (128, 128), force_plan=pid)
+        assert_close(out, ref, f"C2 plan {pid}")
+        assert (out[7, :128].float() == 0).all() and (out[7, -128:].float() == 0).all()
+        p.destroy()
