@@ -28,6 +28,9 @@ COMMON = [
     "-I", os.path.join(HERE, "..", "include"),
 ]
 SOURCES = ["api.cpp", "catalog.cpp", "plan_kernels.hip", "merge_kernel.hip", "attn_kernels.hip"]
+# MFMA accumulators in VGPRs: the softmax reads every score, and AGPR operands
+# would need a v_accvgpr_read per element.
+EXTRA = {"attn_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def write_table_inc():
@@ -42,7 +45,7 @@ def write_table_inc():
 def compile_one(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in ln)

@@ -58,28 +58,50 @@ struct AttnShape {
   static_assert(TQ % 32 == 0 && TKV % 32 == 0 && D % 32 == 0, "shape");
 };
 
-// byte offset of (row, 16B chunk) in the K tile
-template <int TQ, int TKV, int D>
-__device__ __forceinline__ int k_off(int row, int ch) {
-  using S = AttnShape<TQ, TKV, D>;
-  const int sw = kperm(row & 15) & (S::KCH - 1);
-  return row * (D * 2) + ((ch ^ sw) << 4);
+// 16-byte chunk swizzle of a row-major [rows][D] bf16 tile in LDS.  For D=128
+// (16 chunks = 256 B per row) the two 2-bit fields of row%16 are swapped into
+// the chunk index; for D=64 (two rows per 256 B) row/2 is XORed in.  Both the
+// QK^T A-operand reads (ds_read_b128, 16 consecutive permuted rows per lane
+// group) and the PV transposed reads (ds_read_b64_tr_b16, 8 rows x 4 chunks
+// per instruction half) then hit every 16-byte bank group at most the
+// minimum number of times.
+template <int D>
+__device__ __forceinline__ int chunk_swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (row >> 1) & 7;
 }
 
-// byte offset of (d row, 16B key chunk) in the V^T tile
-template <int TQ, int TKV, int D>
-__device__ __forceinline__ int v_off(int drow, int kc) {
-  using S = AttnShape<TQ, TKV, D>;
-  const int sw = (drow / S::VRPB) & (S::VCH - 1);
-  return drow * (TKV * 2) + ((kc ^ sw) << 4);
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int ch) {
+  return row * (D * 2) + ((ch ^ chunk_swz<D>(row)) << 4);
 }
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Value of lane (l ^ 32): v_permlane32_swap exchanges the upper half of one
+// operand with the lower half of the other; swapping x with itself yields
+// {x[l % 32]} in one result and {x[32 + l % 32]} in the other.
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// s_waitcnt vmcnt(0) with the other counters left at their maximum (gfx9
+// encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int TQ, int TKV, int D>
 __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using S = AttnShape<TQ, TKV, D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::KBYTES + S::VBYTES];
-  unsigned char* const kl = smem;
-  unsigned char* const vl = smem + S::KBYTES;
+  constexpr int STAGE = S::KBYTES + S::VBYTES;
+  constexpr int LPW = S::KBYTES / 1024 / S::WAVES;  // 1 KB wave-loads per wave per operand
+  static_assert(LPW >= 1 && LPW * 1024 * S::WAVES == S::KBYTES, "tile/wave split");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_arr[2 * STAGE];
+  unsigned char* const smem = smem_arr;  // lambdas capture this pointer, not the array
 
   // ---- task -------------------------------------------------------------
   int bid = blockIdx.x;
@@ -91,7 +113,7 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   const Task task = a.tasks[bid];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int n = lane & 31;   // query column within the wave (B operand / C column)
   const int hh = lane >> 5;  // lane half
@@ -103,14 +125,11 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   bf16x8 qf[S::DK];
   {
     const bool ok = qrow < N;
-    const __bf16* qp = a.q + head_off + (size_t)qrow * D + 8 * hh;
+    const __bf16* qp = a.q + head_off + (size_t)(ok ? qrow : 0) * D + 8 * hh;
 #pragma unroll
     for (int c = 0; c < S::DK; ++c) {
-      if (ok) {
-        qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
-      } else {
-        for (int i = 0; i < 8; ++i) qf[c][i] = (__bf16)0.0f;
-      }
+      qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
+      if (!ok) qf[c] = bf16x8{};
     }
   }
 
@@ -119,96 +138,23 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   const uint32_t full_kv = (a.coarsen_kv >= 32) ? 0xffffffffu : ((1u << a.coarsen_kv) - 1u);
 
   // ---- online-softmax state (lane-local; l is a half-sum over this lane's keys)
+  // m_run is a reference maximum in log2 units; it is raised only when a score
+  // exceeds it by more than 8, so P stays <= 2^8 and the O rescale is rare.
   float m_run = -INFINITY;
   float l_run = 0.0f;
   f32x16 acc[S::DB];
 #pragma unroll
-  for (int b = 0; b < S::DB; ++b)
-    for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
+  for (int b = 0; b < S::DB; ++b) acc[b] = f32x16{};
 
   const int nsub = 1 << a.sub_log2;
   const int total = (task.end - task.begin) << a.sub_log2;
-
-  // register staging of the next tile
-  u32x4 kreg[S::CPT];
-  u32x4 vreg[S::CPT];
-  const int vdc = tid % S::KCH;      // V loader: 16B column chunk (8 d values)
-  const int vrg = tid / S::KCH;      // V loader: group of CPT consecutive key rows
 
   auto tile_kv0 = [&](int j) -> int {
     const int it = task.begin + (j >> a.sub_log2);
     const int sub = j & (nsub - 1);
     return ((a.tcol[it] << a.sub_log2) + sub) * TKV;
   };
-  auto load_tile = [&](int kv0) {
-    const __bf16* kp = a.k + head_off;
-    const __bf16* vp = a.v + head_off;
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-      const int g = tid + i * S::NT;
-      const int row = g / S::KCH;
-      const int ch = g % S::KCH;
-      const int key = kv0 + row;
-      if (key < N)
-        kreg[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)key * D + ch * 8);
-      else
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-      const int key = kv0 + vrg * S::CPT + i;
-      if (key < N)
-        vreg[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)key * D + vdc * 8);
-      else
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-      const int g = tid + i * S::NT;
-      const int row = g / S::KCH;
-      const int ch = g % S::KCH;
-      *reinterpret_cast<u32x4*>(kl + k_off<TQ, TKV, D>(row, ch)) = kreg[i];
-    }
-    // transpose CPT key rows x 8 d values into 8 d rows x CPT keys
-    const int k0 = vrg * S::CPT;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int drow = vdc * 8 + c;
-      uint32_t packed[(S::CPT + 1) / 2];
-#pragma unroll
-      for (int p = 0; p < (S::CPT + 1) / 2; ++p) {
-        const uint32_t lo = vreg[2 * p][c >> 1];
-        const uint32_t hi = (2 * p + 1 < S::CPT) ? vreg[2 * p + 1][c >> 1] : 0u;
-        packed[p] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      if constexpr (S::CPT >= 8) {
-#pragma unroll
-        for (int q8 = 0; q8 < S::CPT / 8; ++q8) {
-          const int kc = (k0 >> 3) + q8;
-          *reinterpret_cast<u32x4*>(vl + v_off<TQ, TKV, D>(drow, kc)) =
-              u32x4{packed[4 * q8], packed[4 * q8 + 1], packed[4 * q8 + 2], packed[4 * q8 + 3]};
-        }
-      } else if constexpr (S::CPT == 4) {
-        const int kc = k0 >> 3;
-        *reinterpret_cast<u32x2*>(vl + v_off<TQ, TKV, D>(drow, kc) + (k0 & 7) * 2) =
-            u32x2{packed[0], packed[1]};
-      } else if constexpr (S::CPT == 2) {
-        const int kc = k0 >> 3;
-        *reinterpret_cast<uint32_t*>(vl + v_off<TQ, TKV, D>(drow, kc) + (k0 & 7) * 2) = packed[0];
-      } else {
-        static_assert(S::CPT == 1 || S::CPT == 2 || S::CPT == 4 || S::CPT % 8 == 0, "CPT");
-        const int kc = k0 >> 3;
-        *reinterpret_cast<unsigned short*>(vl + v_off<TQ, TKV, D>(drow, kc) + (k0 & 7) * 2) =
-            (unsigned short)(packed[0] & 0xffffu);
-      }
-    }
-  };
-
-  // skip trailing refined sub-tiles that start at or beyond N
-  int j = 0;
-  int kv0 = 0;
+  // skip refined sub-tiles that start at or beyond N
   auto next_valid = [&](int from, int& kvs) -> int {
     int jj = from;
     while (jj < total) {
@@ -218,64 +164,128 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
     }
     return jj;
   };
-  j = next_valid(0, kv0);
-  if (j < total) load_tile(kv0);
+  // Direct-to-LDS fetch of one K and one V tile into stage `buf`: wave-load i
+  // of wave w fills 1 KB of the stage; lane l's 16 bytes land at byte 16*l of
+  // it, so each lane fetches the (row, chunk) that the swizzle places there.
+  // The per-lane byte offsets within a tile are fixed for the whole task.
+  // Rows past N (only in the last tile of a row) are clamped to N-1: finite
+  // data whose scores are masked to -inf.
+  int goff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int slot = (i * S::WAVES + w) * 64 + lane;
+    const int row = slot / S::KCH;
+    goff[i] = row * (D * 2) + (((slot % S::KCH) ^ chunk_swz<D>(row)) << 4);
+  }
+  const char* const kh = reinterpret_cast<const char*>(a.k + head_off);
+  const char* const vh = reinterpret_cast<const char*>(a.v + head_off);
+  auto issue = [&](int kv0, int buf) {
+    unsigned char* kb = smem + buf * STAGE + w * 1024;
+    unsigned char* vb = kb + S::KBYTES;
+    const char* kt = kh + (size_t)kv0 * (D * 2);
+    const char* vt = vh + (size_t)kv0 * (D * 2);
+    if (kv0 + TKV <= N) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        __builtin_amdgcn_global_load_lds(kt + goff[i], (lds_void*)(kb + i * S::WAVES * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + goff[i], (lds_void*)(vb + i * S::WAVES * 1024), 16, 0, 0);
+      }
+    } else {
+      const int last = (N - 1 - kv0) * (D * 2);  // offset of row N-1 within the tile
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int rowoff = goff[i] & ~(D * 2 - 1);
+        const int off = min(rowoff, last) + (goff[i] & (D * 2 - 1));
+        __builtin_amdgcn_global_load_lds(kt + off, (lds_void*)(kb + i * S::WAVES * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + off, (lds_void*)(vb + i * S::WAVES * 1024), 16, 0, 0);
+      }
+    }
+  };
+
+  int kv0 = 0;
+  int j = next_valid(0, kv0);
+  int buf = 0;
+  if (j < total) issue(kv0, 0);
+
+  // Per-lane LDS read bases.  Because the swizzle only XORs the chunk index,
+  // each operand read is lane_base ^ (step << 5 or << 6) plus an immediate row
+  // offset, so the loop needs three base registers and one XOR per step.
+  //   K (A operand of S^T): row st*32 + kperm(n), chunk 2c + hh
+  //   V (A operand of O^T, transposed read): row st*32 + c2*16 + 8*(g>>1) + 4r
+  //     + ((lane&15)>>2), chunk 4b + 2*(g&1) + ((lane&3)>>1), half (lane&1),
+  //     with g = lane/16 and r = 0/1 for key slots 0-3 / 4-7.
+  const int krow0 = kperm(n);
+  const int kbase = krow0 * (D * 2) + 16 * (hh ^ chunk_swz<D>(krow0));
+  const int vgrp = lane >> 4;
+  const int vch0 = 2 * (vgrp & 1) + ((lane & 3) >> 1);
+  const int vrow0 = 8 * (vgrp >> 1) + ((lane & 15) >> 2);
+  const int vbase0 = vrow0 * (D * 2) + 16 * (vch0 ^ chunk_swz<D>(vrow0)) + 8 * (lane & 1);
+  const int vbase1 = (vrow0 + 4) * (D * 2) + 16 * (vch0 ^ chunk_swz<D>(vrow0 + 4)) + 8 * (lane & 1);
 
   while (j < total) {
     const int it = task.begin + (j >> a.sub_log2);
     uint32_t wbits = full_kv;
     if (a.tbits) wbits = (a.tbits[it] >> (sub_row * a.coarsen_kv)) & full_kv;
     const int cur_kv0 = kv0;
-
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();  // tile visible
-
     int kvn = 0;
     const int jn = next_valid(j + 1, kvn);
-    if (jn < total) load_tile(kvn);
+
+    wait_vmcnt0();                 // this wave's loads of tile j have landed
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; tile j-1 fully consumed
+    if (jn < total) issue(kvn, buf ^ 1);
+
+    const lds_u8* kl = (const lds_u8*)(smem + buf * STAGE);
+    const lds_u8* vl = kl + S::KBYTES;
 
     if (wbits != 0u) {
       // ---- S^T = K Q^T ---------------------------------------------------
       f32x16 s[S::NST];
 #pragma unroll
       for (int st = 0; st < S::NST; ++st) {
-        for (int i = 0; i < 16; ++i) s[st][i] = 0.0f;
-        const int krow = st * 32 + kperm(n);
+        s[st] = f32x16{};
 #pragma unroll
         for (int c = 0; c < S::DK; ++c) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + k_off<TQ, TKV, D>(krow, 2 * c + hh));
+          const bf16x8 kf = *(const lds_bf16x8*)(kl + st * 32 * (D * 2) + (kbase ^ (c << 5)));
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[st], 0, 0, 0);
         }
       }
-      // ---- masking: keys >= N and inactive logical blocks of the tile ----
-      const bool ragged = cur_kv0 + TKV > N;
-      if (ragged || wbits != full_kv) {
+      // ---- masking: inactive logical blocks of the tile, keys >= N ---------
+      // A 16-key group (st, v/8) never straddles a logical K/V block (B_KV >=
+      // 16), so membership is one wave-uniform bit test per group.
+      if (wbits != full_kv) {
+#pragma unroll
+        for (int g = 0; g < 2 * S::NST; ++g) {
+          if (!((wbits >> ((16 * g) >> a.bkv_log2)) & 1u)) {
+#pragma unroll
+            for (int v = 0; v < 8; ++v) s[g >> 1][8 * (g & 1) + v] = -INFINITY;
+          }
+        }
+      }
+      if (cur_kv0 + TKV > N) {
+        const int lim = N - cur_kv0 - 8 * hh;  // keys at or past N are masked
 #pragma unroll
         for (int st = 0; st < S::NST; ++st)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int kk = st * 32 + 16 * (v >> 3) + 8 * hh + (v & 7);
-            const bool ok = (cur_kv0 + kk < N) && ((wbits >> (kk >> a.bkv_log2)) & 1u);
-            if (!ok) s[st][v] = -INFINITY;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (st * 32 + 16 * (v >> 3) + (v & 7) >= lim) s[st][v] = -INFINITY;
       }
-      // ---- online softmax (exp2 domain) ----------------------------------
+      // ---- online softmax (exp2 domain, lazy rescale) ---------------------
       float mx = -INFINITY;
 #pragma unroll
       for (int st = 0; st < S::NST; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
+      mx = fmaxf(mx, other_half(mx)) * a.scale_log2;
+      const bool grow = mx > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int b = 0; b < S::DB; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+        for (int b = 0; b < S::DB; ++b) acc[b] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
 
       bf16x8 pf[S::NST][2];
 #pragma unroll
@@ -286,24 +296,29 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
           l_run += p;
           pf[st][v >> 3][v & 7] = (__bf16)p;
         }
-      // ---- O^T += V^T P^T --------------------------------------------------
+      // ---- O^T += V^T P^T; V^T fragments via LDS transpose reads ----------
 #pragma unroll
       for (int b = 0; b < S::DB; ++b)
 #pragma unroll
         for (int st = 0; st < S::NST; ++st)
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-                vl + v_off<TQ, TKV, D>(b * 32 + n, st * 4 + c2 * 2 + hh));
+            const lds_u8* vrow = vl + (st * 32 + c2 * 16) * (D * 2);
+            const bf16x4 lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + (vbase0 ^ (b << 6))));
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + (vbase1 ^ (b << 6))));
+            const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st][c2], acc[b], 0, 0, 0);
           }
     }
+    buf ^= 1;
     j = jn;
     kv0 = kvn;
   }
 
   // ---- epilogue ------------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + other_half(l_run);
   const int r = w * 32 + n;  // row within the query tile
   if (task.slot < 0) {
     if (qrow < N) {
@@ -334,6 +349,7 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
         wo[(size_t)dd * TQ + r] = acc[b][v];
       }
   }
+#endif
 }
 
 template <int TQ, int TKV, int D>
