@@ -2,15 +2,18 @@
 
 One step = one complete BSA request on the GPU: plan creation (mask state,
 statistics transfer, regime lookup, launch preparation) + the attention
-kernels + stream synchronization, with mask, Q, K and V already resident in
-HBM.  Active-block FLOPs are 4*d*|E(M)| (the pages' per-tile accounting over
-effective (query, key) pairs only, clipped at N).
+kernels (+ split-K merge) + stream synchronization, with mask, Q, K and V
+already resident in HBM.  Active-block FLOPs are 4*d*|E(M)|: the per-tile
+accounting of the Tessera paper (section 2.3: QK^T and PV each cost 2*d flops
+per query/key pair) over the effective (query, key) pairs only, clipped at N.
 
 Default workload: the medium request (8 heads, N=8192, d=128, B=(128,128),
-20% i.i.d. + diagonal, one all-active head, one head with two empty query-block
-rows).  --config 3|4|5 runs the other workloads (not the default line).
+20% i.i.d. + diagonal, one all-active head, one head with two empty
+query-block rows).  --config 1|3|4|5 runs the other workloads.  --config 5 is
+the request stream: each step is the next request of 50 (mask and geometry
+re-drawn per request; one Q/K/V set, whose values do not change the work).
 
-Prints one JSON line (rank 0).  Single GPU only.
+Prints one JSON line.  Single GPU only.
 """
 
 import argparse
@@ -25,11 +28,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "BSA request latency (ms, incl. planning) + active-block TFLOP/s, bf16 d=128"
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+WORKLOAD = {1: "tiny", 2: "medium", 3: "wan720p", 4: "hunyuan", 5: "stream"}
 
 
 def effective_pairs(M, BQ, BKV, N):
+    """|E(M)| per head: active blocks weighted by their clipped token extents."""
     import numpy as np
     M = np.asarray(M) != 0
     qsz = np.minimum(BQ, N - np.arange(M.shape[1]) * BQ).astype(np.int64)
@@ -47,43 +51,50 @@ def kernel_source_sha():
 
 
 def load_traffic(workload):
-    """HBM bytes per attention launch from committed rocprofv3 PMC runs, if they
-    were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"attn_traffic_{workload}.json")
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary
+    (profiles/attn_fwd_<workload>_traffic.txt), if it was taken on the current
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
+    kv = {}
     with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                kv[parts[0]] = parts[1]
+    if kv.get("kernel_source_sha") != kernel_source_sha():
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """Time the fp64 oracle (as it stands) on a bounded sample: whole heads, in
-    order, until the budget is spent."""
-    import numpy as np
-
+def cpu_baseline(cfg, budget_s):
+    """Time the fp64 oracle, as it stands, on a bounded sample of the workload:
+    whole heads in order (cycling) until the budget is spent."""
     from oracle import attention as oatt
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    M, BQ, BKV, N = cfg["mask"], cfg["BQ"], cfg["BKV"], cfg["N"]
+    M, BQ, BKV, N, H = cfg["mask"], cfg["BQ"], cfg["BKV"], cfg["N"], cfg["H"]
     _, per_head = effective_pairs(M, BQ, BKV, N)
     t0 = time.perf_counter()
-    heads = 0
-    for h in range(cfg["H"]):
+    n, flops = 0, 0.0
+    while True:
+        h = n % H
         oatt.attention(cfg["q"][h:h + 1], cfg["k"][h:h + 1], cfg["v"][h:h + 1], M[h:h + 1], BQ, BKV)
-        heads += 1
+        flops += 4.0 * cfg["d"] * float(per_head[h])
+        n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    flops = 4.0 * cfg["d"] * float(per_head[:heads].sum())
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 oracle on heads 0..{heads - 1} of {cfg['H']} (all rows), "
-                      f"{dt:.1f} s, active-block flops / wall time",
+            "sample": f"fp64 oracle, {n} whole-head evaluations (heads 0..{min(n, H) - 1} of {H}, "
+                      f"cycling), all rows, {dt:.1f} s; active-block flops / wall time",
             "seconds": round(dt, 2)}
 
 
@@ -93,12 +104,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--requests", type=int, default=50, help="stream length for --config 5")
     ap.add_argument("--force-plan", type=int, default=-1)
+    ap.add_argument("--force-split", type=int, default=-1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
               "(heads would shard across GPUs without communication); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
@@ -111,34 +124,44 @@ def main():
 
     dev = torch.device("cuda:0")
     cfg = gen.config(args.config)
-    H, N, d, BQ, BKV = cfg["H"], cfg["N"], cfg["d"], cfg["BQ"], cfg["BKV"]
-    pairs, _ = effective_pairs(cfg["mask"], BQ, BKV, N)
-    flops = 4.0 * d * pairs
-    Md = torch.from_numpy(cfg["mask"]).to(dev)
+    H, N, d = cfg["H"], cfg["N"], cfg["d"]
     q, k, v = (t.to(dev) for t in (cfg["q"], cfg["k"], cfg["v"]))
     out = torch.empty((H, N, d), dtype=torch.bfloat16, device=dev)
+    # requests: (mask on device, block, flops)
+    reqs = []
+    nreq = args.requests if args.config == 5 else 1
+    for r in range(nreq):
+        if args.config == 5:
+            BQ, BKV, M, _ = gen.request_c5(r)
+        else:
+            BQ, BKV, M = cfg["BQ"], cfg["BKV"], cfg["mask"]
+        pairs, _ = effective_pairs(M, BQ, BKV, N)
+        reqs.append((torch.from_numpy(M).to(dev), (BQ, BKV), 4.0 * d * pairs, pairs))
     torch.cuda.synchronize()
 
-    def request():
-        p = bsa.plan(Md, (BQ, BKV), H, N, d, force_plan=args.force_plan)
+    def request(i):
+        Md, block, _, _ = reqs[i % len(reqs)]
+        p = bsa.plan(Md, block, H, N, d, force_plan=args.force_plan, force_split=args.force_split)
         _, a_ms, m_ms = bsa.run_timed(p, q, k, v, out)
         torch.cuda.synchronize()
         info = p.info
         p.destroy()
         return a_ms, m_ms, info
 
-    for _ in range(args.warmup):
-        request()
+    for i in range(args.warmup):
+        request(i)
     torch.cuda.synchronize()
-    req_ms, attn_ms, merge_ms = [], [], []
-    info = None
+    req_ms, attn_ms, merge_ms, infos = [], [], [], []
+    flops_total = 0.0
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         t0 = time.perf_counter()
-        a_ms, m_ms, info = request()
+        a_ms, m_ms, info = request(args.warmup + i)
         req_ms.append((time.perf_counter() - t0) * 1e3)
         attn_ms.append(a_ms)
         merge_ms.append(m_ms)
+        infos.append(info)
+        flops_total += reqs[(args.warmup + i) % len(reqs)][2]
     torch.cuda.synchronize()
     total_s = time.perf_counter() - t_start
 
@@ -146,13 +169,21 @@ def main():
     med_req = statistics.median(req_ms)
     attn_avg = statistics.mean(attn_ms)
     merge_avg = statistics.mean(merge_ms)
-    achieved = flops / (attn_avg * 1e-3) / 1e12
-    workload = {1: "tiny", 2: "medium", 3: "wan720p", 4: "hunyuan", 5: "stream-r0"}[args.config]
-    traffic = load_traffic(workload)
+    # kernel-side rate: the attention kernel's algorithmic flops / its duration
+    attn_flops = [reqs[(args.warmup + i) % len(reqs)][2] for i in range(args.steps)]
+    achieved = sum(attn_flops) / (sum(attn_ms) * 1e-3) / 1e12
+    workload = WORKLOAD[args.config]
+    info = infos[-1]
     cat = {e["id"]: e for e in bsa.catalog()}
+    Md, block, flops0, pairs0 = reqs[0]
+    if args.config == 5:
+        wl = f"{workload}: {len(reqs)} requests, H={H} N={N} d={d}, B re-drawn per request"
+    else:
+        wl = f"{workload}: H={H} N={N} d={d} B=({block[0]},{block[1]})"
+    planning = [r - a - m for r, a, m in zip(req_ms, attn_ms, merge_ms)]
     res = {
         "metric": METRIC,
-        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "value": flops_total / total_s / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -163,23 +194,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{workload}: H={H} N={N} d={d} B=({BQ},{BKV})",
-                   "global_batch": H, "seq_len": N, "parallelism": "none",
-                   "density": round(info["density"], 4), "active_pairs": pairs,
-                   "active_gflop": round(flops / 1e9, 3)},
+        "config": {"workload": wl, "heads": H, "seq_len": N, "head_dim": d,
+                   "density": round(info["density"], 4), "active_pairs": pairs0,
+                   "active_gflop": round(flops0 / 1e9, 3)},
         "request_ms_median": med_req,
         "request_ms_p95": float(np.percentile(req_ms, 95)),
         "attn_kernel_ms": attn_avg,
         "merge_kernel_ms": merge_avg,
-        "planning_ms": med_req - attn_avg - merge_avg,
-        "planning_share": (med_req - attn_avg - merge_avg) / med_req,
+        "planning_ms_median": statistics.median(planning),
+        "planning_share": statistics.median(planning) / med_req,
         "plan": cat[info["plan_id"]]["name"],
         "regime": info["regime"],
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic},
+                     "traffic": load_traffic(workload)},
     }
-    if args.no_cpu:
+    if args.no_cpu or args.config == 5:
         res["cpu_baseline"] = None
     else:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)

@@ -18,10 +18,11 @@
 //    score accumulators (no cross-lane shuffle) because the K rows are fed to
 //    the QK^T MFMA in a bit-permuted order that makes the result layout equal
 //    the B-operand layout of the PV MFMA.
-//  * Q stays in VGPRs (B operand) for the whole task.  K is staged in LDS
-//    row-major, V transposed (keys contiguous), both with XOR swizzles on 16-
-//    byte chunks so the MFMA operand reads are bank-conflict free.  The next
-//    K/V tile is fetched into registers while the current one is computed.
+//  * Q stays in VGPRs (B operand) for the whole task.  K and V are staged in
+//    LDS row-major with XOR swizzles on 16-byte chunks; K is read with
+//    ds_read_b128 and V with the gfx950 transposing read ds_read_b64_tr_b16,
+//    both bank-conflict free.  Tiles are fetched straight into LDS
+//    (global_load_lds) one stage ahead of the tile being computed.
 //  * Softmax runs in the exp2 domain with the 1/sqrt(d) scale folded into one
 //    FMA per score; a fully masked row never produces NaN (running max -inf is
 //    treated as 0 for the exponent offset) and ends with O = 0.

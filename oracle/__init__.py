@@ -19,9 +19,12 @@ definition written out in float64:
 * ``merge``       split-K partial states and their merge (section 4.3)
 * ``brute``       pure-Python loops for tiny inputs (pins the vectorized code)
 
-Readings of points the pages leave open (scale 1/sqrt(d), zero output for a
-row with no active block, non-causal, ceil-sized mask grid with a ragged last
-block) are listed in the design doc of the repository.
+Readings of points the paper leaves open, used throughout: scores are scaled
+by 1/sqrt(d); a query row with no active block outputs zeros; attention is
+non-causal; the mask grid is ceil(N/B_Q) x ceil(N/B_KV), so the last block of
+each dimension is ragged and keys j >= N never enter the softmax.
+
+Parity pins (no function here is "parity unpinned"): tests/test_oracle_pins.py.
 """
 
 from . import attention, brute, coverage, merge, stats  # noqa: F401
