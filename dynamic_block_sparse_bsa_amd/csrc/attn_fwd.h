@@ -28,12 +28,15 @@
 //    treated as 0 for the exponent offset) and ends with O = 0.
 #pragma once
 
+#include <type_traits>
+
 #include "bsa_internal.h"
 
 namespace bsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -55,6 +58,9 @@ struct AttnShape {
   static constexpr int VRPB = (TKV * 2 >= 128) ? 1 : 128 / (TKV * 2);  // V^T rows per 128 B
   static constexpr int KBYTES = TKV * D * 2;
   static constexpr int VBYTES = TKV * D * 2;
+  // LDS stages of the K/V pipeline: three (two tiles in flight while one is
+  // computed) when three stages of a workgroup fit 48 KB, else two.
+  static constexpr int NSTAGE = (3 * (KBYTES + VBYTES) <= 48 * 1024) ? 3 : 2;
   static_assert(CPT >= 1, "tile too small for the workgroup");
   static_assert(TQ % 32 == 0 && TKV % 32 == 0 && D % 32 == 0, "shape");
 };
@@ -90,9 +96,54 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// s_waitcnt vmcnt(0) with the other counters left at their maximum (gfx9
+// s_waitcnt vmcnt(CNT) with the other counters left at their maximum (gfx9
 // encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <class F, int... Is>
+__device__ __forceinline__ void sfor_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void sfor(F&& f) {
+  sfor_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ds_read_b64_tr_b16 issued from inline assembly.  The compiler's own form of
+// this read is treated as aliasing every in-flight global->LDS transfer and
+// gets an s_waitcnt vmcnt(0) in front of it, which would serialize the K/V
+// prefetch with the PV product.  The K/V stage being read was completed
+// (counted vmcnt wait + workgroup barrier) before any read of it, so the
+// prefetch into another stage cannot alias it.  Results must be fenced with
+// lgkm_wait before use: the compiler does not know they are still in flight.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  if constexpr (OFF < 65536) {
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  } else {
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr + (uint32_t)OFF));
+  }
+  return r;
+}
+
+// s_waitcnt lgkmcnt(CNT) that also ties the given registers, so no use of
+// them can be scheduled above the wait.  LDS operations complete in issue
+// order, so CNT = number of LDS reads issued after the ones being waited for.
+template <int CNT, class Arr>
+__device__ __forceinline__ void lgkm_wait(Arr& regs) {
+  static_assert(CNT >= 0 && CNT < 16, "lgkmcnt field is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(CNT));
+  constexpr int n = sizeof(Arr) / sizeof(u32x2);
+  u32x2* r = reinterpret_cast<u32x2*>(&regs);
+#pragma unroll
+  for (int i = 0; i < n; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+template <int CNT>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(CNT >= 0 && CNT < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((CNT & 15) | ((CNT >> 4) << 14) | 0x0F70);
+}
 
 template <int TQ, int TKV, int D>
 __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
@@ -101,7 +152,8 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int STAGE = S::KBYTES + S::VBYTES;
   constexpr int LPW = S::KBYTES / 1024 / S::WAVES;  // 1 KB wave-loads per wave per operand
   static_assert(LPW >= 1 && LPW * 1024 * S::WAVES == S::KBYTES, "tile/wave split");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_arr[2 * STAGE];
+  constexpr int NSTAGE = S::NSTAGE;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_arr[NSTAGE * STAGE];
   unsigned char* const smem = smem_arr;  // lambdas capture this pointer, not the array
 
   // ---- task -------------------------------------------------------------
@@ -137,33 +189,50 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   // membership: which logical sub-row of a coarsened tile this wave covers
   const int sub_row = (a.coarsen_q > 1) ? (w * 32) / a.bq : 0;
   const uint32_t full_kv = (a.coarsen_kv >= 32) ? 0xffffffffu : ((1u << a.coarsen_kv) - 1u);
+  const uint32_t full_kv_all = 0xffffffffu;  // uncoarsened tiles: every block active
 
   // ---- online-softmax state (lane-local; l is a half-sum over this lane's keys)
   // m_run is a reference maximum in log2 units; it is raised only when a score
   // exceeds it by more than 8, so P stays <= 2^8 and the O rescale is rare.
   float m_run = -INFINITY;
   float l_run = 0.0f;
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
   f32x16 acc[S::DB];
 #pragma unroll
   for (int b = 0; b < S::DB; ++b) acc[b] = f32x16{};
 
-  const int nsub = 1 << a.sub_log2;
-  const int total = (task.end - task.begin) << a.sub_log2;
+  const int sub_log2 = a.sub_log2;
+  const int total = (task.end - task.begin) << sub_log2;
 
-  auto tile_kv0 = [&](int j) -> int {
-    const int it = task.begin + (j >> a.sub_log2);
-    const int sub = j & (nsub - 1);
-    return ((a.tcol[it] << a.sub_log2) + sub) * TKV;
+  // Tile-list window: lane l holds entry wbase + l of the task's column list
+  // (and its membership word), the next window is loaded one window ahead, so
+  // looking an entry up is a v_readlane and never waits on memory inside the
+  // loop.  Indices past the task's last entry are clamped (never used).
+  const bool has_bits = a.tbits != nullptr;
+  const int last_e = task.end - 1;
+  int wbase = task.begin;
+  auto load_win = [&](int base, int& col, uint32_t& bits) {
+    const int e = min(base + lane, last_e);
+    col = a.tcol[e];
+    bits = has_bits ? a.tbits[e] : 0u;
   };
-  // skip refined sub-tiles that start at or beyond N
-  auto next_valid = [&](int from, int& kvs) -> int {
-    int jj = from;
-    while (jj < total) {
-      kvs = tile_kv0(jj);
-      if (kvs < N) break;
-      ++jj;
+  int col_w = 0, col_x = 0;
+  uint32_t bits_w = 0u, bits_x = 0u;
+  if (total > 0) {
+    load_win(wbase, col_w, bits_w);
+    load_win(wbase + 64, col_x, bits_x);
+  }
+  // column and membership of entry e (e never decreases between calls)
+  auto entry = [&](int e, int& col, uint32_t& bits) {
+    if (e - wbase >= 64) {
+      wbase += 64;
+      col_w = col_x;
+      bits_w = bits_x;
+      load_win(wbase + 64, col_x, bits_x);
     }
-    return jj;
+    const int i = e - wbase;
+    col = __builtin_amdgcn_readlane(col_w, i);
+    bits = has_bits ? (uint32_t)__builtin_amdgcn_readlane((int)bits_w, i) : full_kv_all;
   };
   // Direct-to-LDS fetch of one K and one V tile into stage `buf`: wave-load i
   // of wave w fills 1 KB of the stage; lane l's 16 bytes land at byte 16*l of
@@ -203,10 +272,28 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
     }
   };
 
-  int kv0 = 0;
-  int j = next_valid(0, kv0);
-  int buf = 0;
-  if (j < total) issue(kv0, 0);
+  // K/V tile start of sub-tile j (entry begin + (j >> sub_log2)); refined
+  // sub-tiles of the last logical column may start at or past N: they are
+  // neither fetched nor computed.
+  auto lookup = [&](int jj, int& kvs, uint32_t& bits) {
+    int col;
+    entry(task.begin + (jj >> sub_log2), col, bits);
+    kvs = ((col << sub_log2) + (jj & ((1 << sub_log2) - 1))) * TKV;
+  };
+  // Tiles j .. j+NSTAGE-2 are in flight: kvq[i] / bitsq[i] describe tile
+  // j+i (kvq = N: no such tile).
+  int kvq[NSTAGE - 1];
+  uint32_t bitsq[NSTAGE - 1];
+  int j = 0;
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i) {
+    kvq[i] = N;
+    bitsq[i] = 0u;
+    if (i < total) {
+      lookup(i, kvq[i], bitsq[i]);
+      if (kvq[i] < N) issue(kvq[i], i);
+    }
+  }
 
   // Per-lane LDS read bases.  Because the swizzle only XORs the chunk index,
   // each operand read is lane_base ^ (step << 5 or << 6) plus an immediate row
@@ -222,23 +309,44 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   const int vrow0 = 8 * (vgrp >> 1) + ((lane & 15) >> 2);
   const int vbase0 = vrow0 * (D * 2) + 16 * (vch0 ^ chunk_swz<D>(vrow0)) + 8 * (lane & 1);
   const int vbase1 = (vrow0 + 4) * (D * 2) + 16 * (vch0 ^ chunk_swz<D>(vrow0 + 4)) + 8 * (lane & 1);
+  // LDS byte addresses of the transposed V reads per d-block (the stage and
+  // row offsets are added as instruction immediates)
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem_arr;
+  uint32_t vaddr0[S::DB], vaddr1[S::DB];
+#pragma unroll
+  for (int b = 0; b < S::DB; ++b) {
+    vaddr0[b] = lds0 + (uint32_t)(vbase0 ^ (b << 6));
+    vaddr1[b] = lds0 + (uint32_t)(vbase1 ^ (b << 6));
+  }
 
-  while (j < total) {
-    const int it = task.begin + (j >> a.sub_log2);
-    uint32_t wbits = full_kv;
-    if (a.tbits) wbits = (a.tbits[it] >> (sub_row * a.coarsen_kv)) & full_kv;
-    const int cur_kv0 = kv0;
-    int kvn = 0;
-    const int jn = next_valid(j + 1, kvn);
+  // One K/V tile per step; the LDS stage index is a compile-time constant so
+  // every LDS operand read uses an immediate offset (the loop is unrolled by
+  // the two stages).
+  auto step = [&](auto stage_c) {
+    constexpr int buf = decltype(stage_c)::value;
+    const int cur_kv0 = kvq[0];
+    const uint32_t wbits = (bitsq[0] >> (sub_row * a.coarsen_kv)) & full_kv;
+    const int jn = j + NSTAGE - 1;
+    int kvn = N;
+    uint32_t bitsn = 0u;
+    if (jn < total) lookup(jn, kvn, bitsn);
 
-    wait_vmcnt0();                 // this wave's loads of tile j have landed
-    __builtin_amdgcn_s_barrier();  // ... and every wave's; tile j-1 fully consumed
-    if (jn < total) issue(kvn, buf ^ 1);
+    // Wait for this wave's loads of tile j.  Vector-memory loads complete in
+    // issue order, so it is enough that no more than the loads issued after
+    // tile j's (tile j+1's, when three stages are in use) are outstanding.
+    if constexpr (NSTAGE == 3) {
+      if (kvq[1] < N) wait_vmcnt<2 * LPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();  // every wave's tile j landed; tile j-1 fully consumed
+    if (kvn < N) issue(kvn, (buf + NSTAGE - 1) % NSTAGE);
 
     const lds_u8* kl = (const lds_u8*)(smem + buf * STAGE);
     const lds_u8* vl = kl + S::KBYTES;
 
-    if (wbits != 0u) {
+    if (wbits != 0u && cur_kv0 < N) {
       // ---- S^T = K Q^T ---------------------------------------------------
       f32x16 s[S::NST];
 #pragma unroll
@@ -294,28 +402,76 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[st][v], a.scale_log2, -m_use));
-          l_run += p;
           pf[st][v >> 3][v & 7] = (__bf16)p;
         }
-      // ---- O^T += V^T P^T; V^T fragments via LDS transpose reads ----------
+      // l accumulates the bf16-rounded probabilities that enter the PV
+      // product, two per v_dot2 against (1, 1).
 #pragma unroll
-      for (int b = 0; b < S::DB; ++b)
+      for (int st = 0; st < S::NST; ++st)
 #pragma unroll
-        for (int st = 0; st < S::NST; ++st)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const lds_u8* vrow = vl + (st * 32 + c2 * 16) * (D * 2);
-            const bf16x4 lo =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + (vbase0 ^ (b << 6))));
-            const bf16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + (vbase1 ^ (b << 6))));
-            const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st][c2], acc[b], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 pp = {pf[st][h2][2 * e], pf[st][h2][2 * e + 1]};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run, false);
           }
+      // ---- O^T += V^T P^T; V^T fragments via LDS transpose reads ----------
+      // The reads of d-block b+1 are in flight while the MFMAs of block b run.
+      constexpr int VOFF = buf * STAGE + S::KBYTES;  // V tile of this stage
+      constexpr int NVR = S::NST * 2 * 2;           // transposed reads per d-block
+      u32x2 vr[2][S::NST][2][2];
+      auto vread = [&](auto bc, auto slot) {
+        constexpr int b = decltype(bc)::value;
+        sfor<S::NST>([&](auto stc) {
+          constexpr int st = decltype(stc)::value;
+          sfor<2>([&](auto c2c) {
+            constexpr int c2 = decltype(c2c)::value;
+            constexpr int off = VOFF + (st * 32 + c2 * 16) * (D * 2);
+            vr[decltype(slot)::value][st][c2][0] = ds_read_tr16<off>(vaddr0[b]);
+            vr[decltype(slot)::value][st][c2][1] = ds_read_tr16<off>(vaddr1[b]);
+          });
+        });
+      };
+      vread(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      sfor<S::DB>([&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        constexpr int cur = b & 1;
+        if constexpr (b + 1 < S::DB) {
+          vread(std::integral_constant<int, b + 1>{}, std::integral_constant<int, cur ^ 1>{});
+          lgkm_wait<(NVR < 16 ? NVR : 15)>(vr[cur]);  // 15: also waits for one of b+1
+        } else {
+          lgkm_wait<0>(vr[cur]);
+        }
+        sfor<S::NST>([&](auto stc) {
+          constexpr int st = decltype(stc)::value;
+          sfor<2>([&](auto c2c) {
+            constexpr int c2 = decltype(c2c)::value;
+            const u32x4 raw = {vr[cur][st][c2][0][0], vr[cur][st][c2][0][1], vr[cur][st][c2][1][0],
+                               vr[cur][st][c2][1][1]};
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, raw);
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st][c2], acc[b], 0, 0, 0);
+          });
+        });
+      });
     }
-    buf ^= 1;
-    j = jn;
-    kv0 = kvn;
+#pragma unroll
+    for (int i = 0; i + 1 < NSTAGE - 1; ++i) {
+      kvq[i] = kvq[i + 1];
+      bitsq[i] = bitsq[i + 1];
+    }
+    kvq[NSTAGE - 2] = kvn;
+    bitsq[NSTAGE - 2] = bitsn;
+    ++j;
+  };
+  while (true) {
+    if (j >= total) break;
+    step(std::integral_constant<int, 0>{});
+    if (j >= total) break;
+    step(std::integral_constant<int, 1>{});
+    if constexpr (NSTAGE == 3) {
+      if (j >= total) break;
+      step(std::integral_constant<int, 2>{});
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------

@@ -12,11 +12,14 @@ AttnLauncher attn_launcher(int tq, int tkv, int d) {
   BSA_CASE(128, 32, 128)
   BSA_CASE(128, 64, 128)
   BSA_CASE(128, 128, 128)
+  BSA_CASE(256, 32, 128)
+  BSA_CASE(256, 64, 128)
   BSA_CASE(64, 32, 64)
   BSA_CASE(64, 64, 64)
   BSA_CASE(128, 32, 64)
   BSA_CASE(128, 64, 64)
   BSA_CASE(128, 128, 64)
+  BSA_CASE(256, 64, 64)
 #undef BSA_CASE
   return nullptr;
 }
@@ -35,11 +38,14 @@ int attn_wg_per_cu(int tq, int tkv, int d) {
   BSA_CASE(128, 32, 128)
   BSA_CASE(128, 64, 128)
   BSA_CASE(128, 128, 128)
+  BSA_CASE(256, 32, 128)
+  BSA_CASE(256, 64, 128)
   BSA_CASE(64, 32, 64)
   BSA_CASE(64, 64, 64)
   BSA_CASE(128, 32, 64)
   BSA_CASE(128, 64, 64)
   BSA_CASE(128, 128, 64)
+  BSA_CASE(256, 64, 64)
 #undef BSA_CASE
   return 0;
 }

@@ -16,27 +16,31 @@ namespace {
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 std::vector<CatalogEntry> build_catalog() {
-  // kernel tile shapes instantiated for gfx950 (see attn_kernels.hip)
-  static const int shapes[][2] = {{64, 32}, {64, 64}, {128, 32}, {128, 64}, {128, 128}};
+  // kernel tile shapes instantiated for gfx950 (attn_kernels.hip), per head dim
+  struct Shape {
+    int tq, tkv, d;
+  };
+  static const Shape shapes[] = {{64, 32, 128},  {64, 64, 128},  {128, 32, 128}, {128, 64, 128},
+                                 {128, 128, 128}, {256, 32, 128}, {256, 64, 128}, {64, 32, 64},
+                                 {64, 64, 64},   {128, 32, 64},  {128, 64, 64},  {128, 128, 64},
+                                 {256, 64, 64}};
   std::vector<CatalogEntry> c;
-  for (int d : {128, 64}) {
-    for (auto& s : shapes) {
-      // organizations: no split; split-K balance rule; split-K + per-XCD grouping
-      const int orgs[][2] = {{1, 0}, {0, 0}, {1, 1}};
-      for (auto& o : orgs) {
-        CatalogEntry e;
-        e.id = (int)c.size();
-        e.tq = s[0];
-        e.tkv = s[1];
-        e.d = d;
-        e.split = o[0];
-        e.xcd_remap = o[1];
-        char buf[48];
-        std::snprintf(buf, sizeof buf, "T%dx%d_d%d_%s%s", e.tq, e.tkv, d, e.split ? "splitk" : "nosplit",
-                      e.xcd_remap ? "_xcd" : "");
-        e.name = buf;
-        c.push_back(e);
-      }
+  for (const Shape& s : shapes) {
+    // organizations: split-K balance rule; no split; split-K + per-XCD grouping
+    const int orgs[][2] = {{1, 0}, {0, 0}, {1, 1}};
+    for (auto& o : orgs) {
+      CatalogEntry e;
+      e.id = (int)c.size();
+      e.tq = s.tq;
+      e.tkv = s.tkv;
+      e.d = s.d;
+      e.split = o[0];
+      e.xcd_remap = o[1];
+      char buf[48];
+      std::snprintf(buf, sizeof buf, "T%dx%d_d%d_%s%s", e.tq, e.tkv, e.d, e.split ? "splitk" : "nosplit",
+                    e.xcd_remap ? "_xcd" : "");
+      e.name = buf;
+      c.push_back(e);
     }
   }
   return c;
