@@ -11,7 +11,7 @@ the import of any entry point raises.
 import ctypes
 import os
 
-__all__ = ["BsaError", "Plan", "plan", "run", "run_timed", "catalog", "select", "eligible",
+__all__ = ["BsaError", "Plan", "plan", "run", "run_timed", "catalog", "select", "eligible", "base_plan",
            "table_load", "table_version", "catalog_hash", "library_path"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +44,7 @@ class PlanInfo(ctypes.Structure):
         [(n, ctypes.c_int64) for n in (
             "nnz_blocks", "n_tile_rows", "n_items", "n_tasks", "grid", "workspace_bytes",
             "long_run_blocks")] + \
-        [(n, ctypes.c_double) for n in ("density", "run_coverage", "host_select_us")]
+        [(n, ctypes.c_double) for n in ("density", "run_coverage", "row_skew", "host_select_us")]
 
 
 class CatalogEntry(ctypes.Structure):
@@ -78,14 +78,16 @@ def _load():
     L.bsa_catalog_get.argtypes = [i32, ctypes.POINTER(CatalogEntry)]
     L.bsa_plan_eligible.argtypes = [i32, ctypes.POINTER(Request), ctypes.POINTER(i32)]
     L.bsa_select.argtypes = [ctypes.POINTER(Request), ctypes.c_double, ctypes.c_double,
-                             ctypes.POINTER(i32), ctypes.POINTER(i32)]
+                             ctypes.c_double, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.bsa_table_load.argtypes = [ctypes.c_char_p]
+    L.bsa_base_plan.argtypes = [ctypes.POINTER(Request), ctypes.POINTER(i32)]
     for f in ("bsa_table_version", "bsa_catalog_hash", "bsa_status_string", "bsa_last_error"):
         getattr(L, f).restype = ctypes.c_char_p
     L.bsa_status_string.argtypes = [i32]
     for f in ("bsa_plan_create", "bsa_run", "bsa_run_timed", "bsa_plan_destroy",
               "bsa_plan_get_info", "bsa_plan_export_tiles", "bsa_plan_export_csr",
-              "bsa_catalog_get", "bsa_plan_eligible", "bsa_select", "bsa_table_load"):
+              "bsa_catalog_get", "bsa_plan_eligible", "bsa_select", "bsa_table_load",
+              "bsa_base_plan"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -229,13 +231,21 @@ def eligible(plan_id, H, N, d, block, workspace_limit=0):
     return bool(out.value)
 
 
-def select(H, N, d, block, density, run_coverage):
+def select(H, N, d, block, density, run_coverage, row_skew=1.0):
     """Host-only regime lookup + ranked fallback: (plan_id, regime)."""
     r = _request(H, N, d, block, None)
     pid, reg = ctypes.c_int32(-1), ctypes.c_int32(-1)
-    _check(_load().bsa_select(ctypes.byref(r), density, run_coverage, ctypes.byref(pid),
+    _check(_load().bsa_select(ctypes.byref(r), density, run_coverage, row_skew, ctypes.byref(pid),
                               ctypes.byref(reg)))
     return pid.value, reg.value
+
+
+def base_plan(H, N, d, block):
+    """Catalog id of the request key's base plan (host only)."""
+    r = _request(H, N, d, block, None)
+    pid = ctypes.c_int32(-1)
+    _check(_load().bsa_base_plan(ctypes.byref(r), ctypes.byref(pid)))
+    return pid.value
 
 
 def table_load(path):

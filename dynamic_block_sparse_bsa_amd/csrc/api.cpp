@@ -204,19 +204,21 @@ struct bsa_plan {
   bool coarse = false;
   MaskStats stats{};
   bsa_plan_info info{};
-  DevBuf stats_dev, row_cnt, row_ptr, cols, trow_cnt, trow_ptr_buf, tcol_buf, tbits_buf, parts, slots,
-      task_off, slot_off, tasks, ws;
+  DevBuf stats_dev, row_cnt, row_ptr, row_part, cols, trow_cnt, trow_ptr_buf, tcol_buf, tbits_buf, parts,
+      slot_off, tasks, ws;
   const int32_t* trow_ptr = nullptr;
   const int32_t* tcol = nullptr;
   const uint32_t* tbits = nullptr;
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  hipEvent_t done = nullptr;  // recorded after the plan's latest stream work (create or run)
 
   ~bsa_plan() {
-    for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &cols, &trow_cnt, &trow_ptr_buf, &tcol_buf,
-                      &tbits_buf, &parts, &slots, &task_off, &slot_off, &tasks, &ws})
+    for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &row_part, &cols, &trow_cnt, &trow_ptr_buf, &tcol_buf,
+                      &tbits_buf, &parts, &slot_off, &tasks, &ws})
       pool_release(b);
     for (auto& e : ev)
       if (e) (void)hipEventDestroy(e);
+    if (done) (void)hipEventDestroy(done);
   }
 };
 
@@ -309,10 +311,10 @@ bsa_status bsa_plan_eligible(int32_t id, const bsa_request* req, int32_t* out) {
   return BSA_OK;
 }
 
-bsa_status bsa_select(const bsa_request* req, double density, double run_coverage, int32_t* plan_id,
-                      int32_t* regime) {
+bsa_status bsa_select(const bsa_request* req, double density, double run_coverage, double row_skew,
+                      int32_t* plan_id, int32_t* regime) {
   if (!req || !plan_id || !regime) return fail(BSA_ERR_INVALID_ARG, "NULL argument to bsa_select");
-  Selection s = lookup(*req, density, run_coverage);
+  Selection s = lookup(*req, density, run_coverage, row_skew);
   *regime = s.regime;
   for (int c : s.candidates) {
     if (eligible(catalog()[c], *req, -1, nullptr)) {
@@ -324,6 +326,15 @@ bsa_status bsa_select(const bsa_request* req, double density, double run_coverag
   return fail(BSA_ERR_UNSUPPORTED, "no eligible plan for B=(%d,%d) d=%d", req->block_q, req->block_kv, req->d);
 }
 
+bsa_status bsa_base_plan(const bsa_request* req, int32_t* plan_id) {
+  if (!req || !plan_id) return fail(BSA_ERR_INVALID_ARG, "NULL argument to bsa_base_plan");
+  *plan_id = base_plan(*req);
+  if (*plan_id < 0)
+    return fail(BSA_ERR_UNSUPPORTED, "no eligible base plan for B=(%d,%d) d=%d", req->block_q, req->block_kv,
+                req->d);
+  return BSA_OK;
+}
+
 bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out) {
   if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
@@ -331,6 +342,15 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   if (vs != BSA_OK) return vs;
   hipStream_t s = (hipStream_t)stream;
   std::unique_ptr<bsa_plan> p(new bsa_plan());
+  // On an error return, kernels already queued may still use the plan's
+  // buffers: wait for the stream before they go back to the cache.
+  struct DrainOnError {
+    std::unique_ptr<bsa_plan>& plan;
+    hipStream_t stream;
+    ~DrainOnError() {
+      if (plan) (void)hipStreamSynchronize(stream);
+    }
+  } drain{p, s};
   p->req = *req;
   p->req.mask = nullptr;  // not retained
   HIP_TRY(hipGetDevice(&p->dev));
@@ -343,10 +363,12 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   HIP_TRY(pool_alloc(p->dev, sizeof(MaskStats), &p->stats_dev));
   HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
   HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nrows + 1), &p->row_ptr));
+  const int npart = row_count_blocks(nrows);
+  HIP_TRY(pool_alloc(p->dev, sizeof(RowPartial) * (size_t)npart, &p->row_part));
   MaskStats* dst = (MaskStats*)p->stats_dev.ptr;
-  HIP_TRY(launch_zero_stats(dst, s));
-  HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, dst, s));
-  HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, &dst->nnz, s));
+  RowPartial* part = (RowPartial*)p->row_part.ptr;
+  HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, part, s));
+  HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, s));
   MaskStats* host = pinned_stats();
   if (!host) return fail(BSA_ERR_NO_MEMORY, "pinned host allocation failed");
   HIP_TRY(hipMemcpyAsync(host, dst, sizeof(MaskStats), hipMemcpyDeviceToHost, s));
@@ -355,6 +377,7 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   const double total_blocks = (double)r.H * p->nqb * p->nkb;
   const double density = p->stats.nnz / total_blocks;
   const double runcov = p->stats.nnz ? (double)p->stats.long_run / (double)p->stats.nnz : 0.0;
+  const double skew = p->stats.nnz ? (double)p->stats.max_row_nnz * nrows / (double)p->stats.nnz : 0.0;
 
   // ---- regime lookup and ranked fallback ------------------------------------
   const auto t0 = std::chrono::steady_clock::now();
@@ -363,7 +386,7 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     sel.regime = -2;
     sel.candidates = {r.force_plan};
   } else {
-    sel = lookup(r, density, runcov);
+    sel = lookup(r, density, runcov, skew);
   }
   const CatalogEntry* chosen = nullptr;
   PlanShape shape;
@@ -403,7 +426,8 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     HIP_TRY(pool_alloc(p->dev, sizeof(uint32_t) * std::max<size_t>(nnz, 1), &p->tbits_buf));
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
                            ntc, (int32_t*)p->trow_cnt.ptr, nullptr, nullptr, nullptr, s));
-    HIP_TRY(launch_scan((int32_t*)p->trow_cnt.ptr, (int32_t*)p->trow_ptr_buf.ptr, ntrows, nullptr, s));
+    HIP_TRY(launch_scan((int32_t*)p->trow_cnt.ptr, (int32_t*)p->trow_ptr_buf.ptr, ntrows, nullptr, 0, nullptr,
+                        s));
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
                            ntc, nullptr, (int32_t*)p->trow_ptr_buf.ptr, (int32_t*)p->tcol_buf.ptr,
                            (uint32_t*)p->tbits_buf.ptr, s));
@@ -420,16 +444,10 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   // ---- tasks and split-K partitions -----------------------------------------
   const int64_t nqt = shape.nqt;
   HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->parts));
-  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->slots));
-  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nqt + 1), &p->task_off));
-  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nqt + 1), &p->slot_off));
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->slot_off));
   HIP_TRY(pool_alloc(p->dev, sizeof(Task) * (size_t)std::max<int64_t>(shape.tasks_upper, 1), &p->tasks));
-  HIP_TRY(launch_task_count(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split,
-                            (int32_t*)p->parts.ptr, (int32_t*)p->slots.ptr, s));
-  HIP_TRY(launch_scan((int32_t*)p->parts.ptr, (int32_t*)p->task_off.ptr, (int32_t)nqt, &dst->n_tasks, s));
-  HIP_TRY(launch_scan((int32_t*)p->slots.ptr, (int32_t*)p->slot_off.ptr, (int32_t)nqt, nullptr, s));
-  HIP_TRY(launch_task_write(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, (int32_t*)p->parts.ptr,
-                            (int32_t*)p->task_off.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr, s));
+  HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split,
+                       (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr, dst, s));
   if (shape.slots_upper > 0) HIP_TRY(pool_alloc(p->dev, (size_t)shape.ws_bytes, &p->ws));
   p->grid = chosen->xcd_remap ? cdiv(shape.tasks_upper, 8) * 8 : shape.tasks_upper;
   if (p->grid < 1) p->grid = chosen->xcd_remap ? 8 : 1;
@@ -456,7 +474,10 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   in.long_run_blocks = (int64_t)p->stats.long_run;
   in.density = density;
   in.run_coverage = runcov;
+  in.row_skew = skew;
   in.host_select_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+  HIP_TRY(hipEventCreateWithFlags(&p->done, hipEventDisableTiming));
+  HIP_TRY(hipEventRecord(p->done, s));
   *out = p.release();
   return BSA_OK;
 }
@@ -521,6 +542,7 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
     m.d = e.d;
     HIP_TRY(launch_merge(m, (int32_t)p->shape.nqt, s));
   }
+  HIP_TRY(hipEventRecord(mp->done, s));
   if (timed) {
     HIP_TRY(hipEventRecord(mp->ev[2], s));
     HIP_TRY(hipEventSynchronize(mp->ev[2]));
@@ -544,9 +566,11 @@ bsa_status bsa_run_timed(const bsa_plan* p, const void* q, const void* k, const 
 
 bsa_status bsa_plan_destroy(bsa_plan* p) {
   if (!p) return BSA_OK;
-  hipError_t e = hipDeviceSynchronize();
+  // wait for the plan's latest stream work (its creation or last run) before
+  // its device memory returns to the cache
+  hipError_t e = p->done ? hipEventSynchronize(p->done) : hipDeviceSynchronize();
   delete p;
-  if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "waiting for the plan's work: %s", hipGetErrorString(e));
   return BSA_OK;
 }
 

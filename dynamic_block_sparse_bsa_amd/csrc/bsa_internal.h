@@ -31,6 +31,13 @@ struct MaskStats {
   unsigned long long n_tasks;        // tasks written by the task builder
 };
 
+// Per-workgroup partial statistics of the row-count kernel.
+struct RowPartial {
+  unsigned long long long_run;
+  unsigned int max_row;
+  unsigned int empty;
+};
+
 // Arguments of the attention mainloop kernels.
 struct AttnArgs {
   const __bf16* q;
@@ -71,23 +78,21 @@ struct MergeArgs {
 // Kernel launchers (defined in the .hip translation units).
 using AttnLauncher = hipError_t (*)(const AttnArgs&, int grid, hipStream_t);
 
-hipError_t launch_zero_stats(MaskStats* st, hipStream_t s);
+int row_count_blocks(int32_t nrows);  // workgroups (= partials) of the row-count kernel
 hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_cnt,
-                            MaskStats* st, hipStream_t s);
-hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, unsigned long long* total,
-                       hipStream_t s);
+                            RowPartial* part, hipStream_t s);
+// Exclusive scan; with st non-null also completes the mask statistics.
+hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPartial* part,
+                       int32_t npart, MaskStats* st, hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
                           int32_t* cols, hipStream_t s);
 hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,
                           int32_t nkb, int32_t cq, int32_t ckv, int32_t ntr, int32_t ntc,
                           int32_t* trow_cnt, const int32_t* trow_ptr, int32_t* tcol,
                           uint32_t* tbits, hipStream_t s);
-hipError_t launch_task_count(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
-                             int32_t refine_q, int32_t split, int32_t* parts, int32_t* slots,
-                             hipStream_t s);
-hipError_t launch_task_write(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
-                             int32_t refine_q, const int32_t* parts, const int32_t* task_off,
-                             const int32_t* slot_off, Task* tasks, hipStream_t s);
+hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
+                        int32_t refine_q, int32_t split, int32_t* parts, int32_t* slot_base,
+                        Task* tasks, MaskStats* st, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s);
 
 // Attention kernel table: returns nullptr when (tq, tkv, d) has no kernel.

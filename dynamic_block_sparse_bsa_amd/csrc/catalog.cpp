@@ -47,12 +47,12 @@ std::vector<CatalogEntry> build_catalog() {
 }
 
 struct Bounds {
-  std::vector<double> H, N, density, runcov;
+  std::vector<double> H, N, density, runcov, skew;
 };
 
 struct Regime {
   int bq, bkv, d;
-  int hb, nb, db, rb;  // bucket index per feature, -1 = any
+  int hb, nb, db, rb, sb;  // bucket index per feature, -1 = any
   std::vector<int> ranking;
 };
 
@@ -152,18 +152,19 @@ int base_plan(const bsa_request& r) {
   return best;
 }
 
-Selection lookup(const bsa_request& r, double density, double run_coverage) {
+Selection lookup(const bsa_request& r, double density, double run_coverage, double row_skew) {
   std::lock_guard<std::mutex> lk(g_table_mu);
   ensure_table();
   Selection s;
   const Table& t = g_table;
   const int hb = bucket(t.bounds.H, r.H), nb = bucket(t.bounds.N, r.N);
   const int db = bucket(t.bounds.density, density), rb = bucket(t.bounds.runcov, run_coverage);
+  const int sb = bucket(t.bounds.skew, row_skew);
   for (size_t i = 0; i < t.regimes.size(); ++i) {
     const Regime& g = t.regimes[i];
     if (g.bq != r.block_q || g.bkv != r.block_kv || g.d != r.d) continue;
     if ((g.hb >= 0 && g.hb != hb) || (g.nb >= 0 && g.nb != nb) || (g.db >= 0 && g.db != db) ||
-        (g.rb >= 0 && g.rb != rb))
+        (g.rb >= 0 && g.rb != rb) || (g.sb >= 0 && g.sb != sb))
       continue;
     s.regime = (int)i;
     s.candidates = g.ranking;
@@ -180,7 +181,8 @@ Selection lookup(const bsa_request& r, double density, double run_coverage) {
 //   arch gfx950
 //   catalog <hex hash of the catalog>
 //   bounds <H|N|density|run_coverage> v1 v2 ...     (bucket k: b[k-1] <= x < b[k])
-//   regime <B_Q> <B_KV> <d> <hb> <nb> <db> <rb> : <plan name> <plan name> ...
+//   bounds row_skew v1 ...   (row skew = max row count * rows / active blocks)
+//   regime <B_Q> <B_KV> <d> <hb> <nb> <db> <rb> <sb> : <plan name> <plan name> ...
 // Lines starting with '#' are comments; '*' matches any bucket.
 namespace {
 bsa_status parse_table(const std::string& text, Table* out, std::string* err) {
@@ -229,10 +231,11 @@ bsa_status parse_table(const std::string& text, Table* out, std::string* err) {
       else if (f == "N") t.bounds.N = v;
       else if (f == "density") t.bounds.density = v;
       else if (f == "run_coverage") t.bounds.runcov = v;
+      else if (f == "row_skew") t.bounds.skew = v;
       else return fail("unknown feature " + f);
     } else if (kw == "regime") {
       Regime g;
-      std::string tok[7];
+      std::string tok[8];
       for (auto& s : tok) ls >> s;
       auto num = [&](const std::string& s, int* out) {
         if (s == "*") {
@@ -245,8 +248,8 @@ bsa_status parse_table(const std::string& text, Table* out, std::string* err) {
         *out = (int)v;
         return true;
       };
-      int* outs[7] = {&g.bq, &g.bkv, &g.d, &g.hb, &g.nb, &g.db, &g.rb};
-      for (int i = 0; i < 7; ++i)
+      int* outs[8] = {&g.bq, &g.bkv, &g.d, &g.hb, &g.nb, &g.db, &g.rb, &g.sb};
+      for (int i = 0; i < 8; ++i)
         if (!num(tok[i], outs[i])) return fail("bad regime field '" + tok[i] + "'");
       std::string colon;
       ls >> colon;

@@ -55,8 +55,8 @@ struct Selection {
 };
 
 // Regime lookup (stage 1: key = (arch, B, dtype, d, layout); stage 2: feature
-// buckets of H, N, density and run coverage).
-Selection lookup(const bsa_request& r, double density, double run_coverage);
+// buckets of H, N, density, run coverage and row skew).
+Selection lookup(const bsa_request& r, double density, double run_coverage, double row_skew);
 
 bsa_status table_load_file(const char* path, std::string* err);
 bsa_status table_load_text(const std::string& text, std::string* err);

@@ -8,8 +8,10 @@
 // derived from the shared block-CSR (tile membership for Coarsened plans,
 // split-K partition information, traversal descriptors).
 //
-// All kernels are wave64; integer reductions use ballot/popcount and integer
+// All kernels are wave64; reductions use ballot/popcount, LDS and integer
 // atomics only, so every result is deterministic.
+#include <algorithm>
+
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -23,77 +25,132 @@ __device__ inline unsigned prefix_count(unsigned long long ballot) {
                                    __builtin_amdgcn_mbcnt_lo((unsigned)ballot, 0u));
 }
 
-__global__ void k_zero_stats(MaskStats* st) {
+// Active count per query-block row, and per-workgroup partial statistics:
+// active blocks lying in runs of length >= 2 (an active block whose left or
+// right neighbour in the row is active; paper section 5.1), the largest row
+// count and the number of empty rows.  Each wave walks whole rows
+// (grid-stride), one byte per lane per 64-column chunk; the neighbour tests
+// are shifts of the chunk's ballot, carried across chunk boundaries.
+__global__ __launch_bounds__(256) void k_row_count(const uint8_t* __restrict__ mask, int32_t nrows,
+                                                   int32_t nkb, int32_t* __restrict__ row_cnt,
+                                                   RowPartial* __restrict__ part) {
+  __shared__ unsigned long long s_long[4];
+  __shared__ unsigned s_max[4], s_empty[4];
+  const unsigned l = lane_id();
+  const int wv = threadIdx.x >> 6;
+  unsigned long long lng_w = 0;
+  unsigned max_w = 0, empty_w = 0;
+  const int nwaves = gridDim.x * 4;
+  for (int row = blockIdx.x * 4 + wv; row < nrows; row += nwaves) {
+    const uint8_t* r = mask + (size_t)row * nkb;
+    unsigned cnt = 0, lng = 0;
+    unsigned long long prev = 0;  // ballot of the previous chunk (bit 63 = its last column)
+    unsigned long long cur = __ballot((int)l < nkb && r[l] != 0);
+    for (int base = 0; base < nkb; base += 64) {
+      const int p = base + 64 + (int)l;
+      const unsigned long long next = (base + 64 < nkb) ? __ballot(p < nkb && r[p] != 0) : 0ull;
+      const unsigned long long left = (cur << 1) | (prev >> 63);
+      const unsigned long long right = (cur >> 1) | (next << 63);
+      cnt += __popcll(cur);
+      lng += __popcll(cur & (left | right));
+      prev = cur;
+      cur = next;
+    }
+    if (l == 0) row_cnt[row] = (int32_t)cnt;
+    lng_w += lng;
+    max_w = max(max_w, cnt);
+    empty_w += (cnt == 0);
+  }
+  if (l == 0) {
+    s_long[wv] = lng_w;
+    s_max[wv] = max_w;
+    s_empty[wv] = empty_w;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    st->nnz = 0;
-    st->long_run = 0;
-    st->max_row_nnz = 0;
-    st->empty_rows = 0;
-    st->n_tasks = 0;
+    RowPartial rp;
+    rp.long_run = s_long[0] + s_long[1] + s_long[2] + s_long[3];
+    rp.max_row = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+    rp.empty = s_empty[0] + s_empty[1] + s_empty[2] + s_empty[3];
+    part[blockIdx.x] = rp;
   }
 }
 
-// One wave per query-block row: active count, and the number of active blocks
-// whose left or right neighbour in the row is active (exactly the blocks that
-// lie in runs of length >= 2, paper section 5.1).
-__global__ __launch_bounds__(256) void k_row_count(const uint8_t* __restrict__ mask, int32_t nrows,
-                                                   int32_t nkb, int32_t* __restrict__ row_cnt,
-                                                   MaskStats* st) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wave >= nrows) return;
-  const unsigned l = lane_id();
-  const uint8_t* row = mask + (size_t)wave * nkb;
-  unsigned cnt = 0, lng = 0;
-  for (int base = 0; base < nkb; base += 64) {
-    const int p = base + (int)l;
-    bool a = false, left = false, right = false;
-    if (p < nkb) {
-      a = row[p] != 0;
-      left = p > 0 && row[p - 1] != 0;
-      right = p + 1 < nkb && row[p + 1] != 0;
-    }
-    const unsigned long long ba = __ballot(a);
-    const unsigned long long bl = __ballot(a && (left || right));
-    cnt += __popcll(ba);
-    lng += __popcll(bl);
+// Block-wide exclusive scan of one int32 per thread (1024 threads); returns
+// the exclusive prefix and sets *tot to the block total.
+__device__ int32_t block_scan(int32_t v, int32_t* lds, int32_t* tot) {
+  const int t = threadIdx.x;
+  lds[t] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
+    const int32_t x = t >= off ? lds[t - off] : 0;
+    __syncthreads();
+    lds[t] += x;
+    __syncthreads();
   }
-  if (l == 0) {
-    row_cnt[wave] = (int32_t)cnt;
-    if (lng) atomicAdd(&st->long_run, (unsigned long long)lng);
-    atomicMax(&st->max_row_nnz, cnt);
-    if (cnt == 0) atomicAdd(&st->empty_rows, 1u);
-  }
+  const int32_t incl = lds[t];
+  *tot = lds[1023];
+  __syncthreads();
+  return incl - v;
 }
 
 // Exclusive scan of n int32 values by one workgroup of 1024 threads; out has
-// n + 1 entries (out[n] = total); *total (if non-null) receives the total.
+// n + 1 entries (out[n] = total).  The input is walked in coalesced tiles of
+// 4096 values (four consecutive values per thread).  With `st` non-null the
+// kernel also completes the mask statistics: nnz = total, the reduction of
+// the row-count kernel's `npart` partials, and n_tasks = 0.
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
                                                int32_t* __restrict__ out, int32_t n,
-                                               unsigned long long* total) {
-  __shared__ int32_t part[1024];
+                                               const RowPartial* __restrict__ part, int32_t npart,
+                                               MaskStats* st) {
+  __shared__ int32_t lds[1024];
   const int t = threadIdx.x;
-  const int per = (n + 1023) / 1024;
-  const int b = t * per;
-  const int e = min(n, b + per);
-  int32_t s = 0;
-  for (int i = b; i < e; ++i) s += in[i];
-  part[t] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
-  for (int off = 1; off < 1024; off <<= 1) {
-    int32_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  int32_t carry = 0;
+  for (int base = 0; base < n; base += 4096) {
+    const int i0 = base + 4 * t;
+    int32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = (i0 + k < n) ? in[i0 + k] : 0;
+    int32_t tot;
+    int32_t run = carry + block_scan(v[0] + v[1] + v[2] + v[3], lds, &tot);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (i0 + k < n) out[i0 + k] = run;
+      run += v[k];
+    }
+    carry += tot;
   }
-  int32_t run = t > 0 ? part[t - 1] : 0;
-  for (int i = b; i < e; ++i) {
-    out[i] = run;
-    run += in[i];
-  }
-  if (t == 1023) {
-    out[n] = part[1023];
-    if (total) *total = (unsigned long long)part[1023];
+  if (t == 0) out[n] = carry;
+  if (st) {
+    // reduce the partial statistics: thread t folds partials t, t+1024, ...
+    __shared__ unsigned long long s_long[1024];
+    __shared__ unsigned s_max[1024], s_empty[1024];
+    unsigned long long lg = 0;
+    unsigned mx = 0, em = 0;
+    for (int i = t; i < npart; i += 1024) {
+      lg += part[i].long_run;
+      mx = max(mx, part[i].max_row);
+      em += part[i].empty;
+    }
+    s_long[t] = lg;
+    s_max[t] = mx;
+    s_empty[t] = em;
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+      if (t < off) {
+        s_long[t] += s_long[t + off];
+        s_max[t] = max(s_max[t], s_max[t + off]);
+        s_empty[t] += s_empty[t + off];
+      }
+      __syncthreads();
+    }
+    if (t == 0) {
+      st->nnz = (unsigned long long)carry;
+      st->long_run = s_long[0];
+      st->max_row_nnz = s_max[0];
+      st->empty_rows = s_empty[0];
+      st->n_tasks = 0;
+    }
   }
 }
 
@@ -181,74 +238,90 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
   }
 }
 
-// Split-K partition count per query tile (paper section 4.3, "Split-K"):
-// a query tile whose tile-list row holds more than `split` entries is cut into
-// ceil(n / split) partitions of near-equal size; split == 0 never splits.
-// parts[q] = partitions (>= 1; a tile with no entries still gets one task that
-// writes zeros), slots[q] = workspace slots (parts if split, else 0).
-__global__ __launch_bounds__(256) void k_task_count(const int32_t* __restrict__ trow_ptr,
-                                                    int32_t H, int32_t nqt_head, int32_t ntr,
-                                                    int32_t refine_q, int32_t split,
-                                                    int32_t* __restrict__ parts,
-                                                    int32_t* __restrict__ slots) {
-  const int g = blockIdx.x * 256 + threadIdx.x;
-  if (g >= H * nqt_head) return;
-  const int h = g / nqt_head;
-  const int qt = g - h * nqt_head;
-  const int tr = qt / refine_q;
-  const int n = trow_ptr[h * ntr + tr + 1] - trow_ptr[h * ntr + tr];
-  const int p = (split > 0 && n > split) ? (n + split - 1) / split : 1;
-  parts[g] = p;
-  slots[g] = p > 1 ? p : 0;
-}
 
-__global__ __launch_bounds__(256) void k_task_write(const int32_t* __restrict__ trow_ptr,
-                                                    int32_t H, int32_t nqt_head, int32_t ntr,
-                                                    int32_t refine_q,
-                                                    const int32_t* __restrict__ parts,
-                                                    const int32_t* __restrict__ task_off,
-                                                    const int32_t* __restrict__ slot_off,
-                                                    Task* __restrict__ tasks) {
-  const int g = blockIdx.x * 256 + threadIdx.x;
-  if (g >= H * nqt_head) return;
-  const int h = g / nqt_head;
-  const int qt = g - h * nqt_head;
-  const int tr = qt / refine_q;
-  const int b = trow_ptr[h * ntr + tr];
-  const int e = trow_ptr[h * ntr + tr + 1];
-  const int p = parts[g];
-  const int n = e - b;
-  const int chunk = (n + p - 1) / p;
-  const int t0 = task_off[g];
-  for (int i = 0; i < p; ++i) {
-    Task t;
-    t.head = h;
-    t.qtile = qt;
-    t.begin = min(e, b + i * chunk);
-    t.end = min(e, b + (i + 1) * chunk);
-    t.slot = p > 1 ? slot_off[g] + i : -1;
-    t.pad0 = t.pad1 = t.pad2 = 0;
-    tasks[t0 + i] = t;
+// Task list (paper section 4.3, "Grouping and traversal" and "Split-K"), one
+// workgroup: query tile g = h * nqt_head + qt traverses tile-list row
+// h * ntr + qt / refine_q.  A row with more than `split` entries is cut into
+// ceil(n / split) contiguous partitions of near-equal size (split == 0 never
+// splits); every query tile gets at least one task, so rows without entries
+// still write zeros.  Writes, per query tile, its partition count and first
+// workspace slot (for the merge kernel), the tasks in query-tile order, and
+// the task count into st->n_tasks.
+__global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow_ptr, int32_t H,
+                                                int32_t nqt_head, int32_t ntr, int32_t refine_q,
+                                                int32_t split, int32_t* __restrict__ parts,
+                                                int32_t* __restrict__ slot_base,
+                                                Task* __restrict__ tasks, MaskStats* st) {
+  __shared__ int32_t lds[1024];
+  const int t = threadIdx.x;
+  const int nqt = H * nqt_head;
+  int32_t carry_t = 0, carry_s = 0;
+  for (int base = 0; base < nqt; base += 4096) {
+    const int g0 = base + 4 * t;
+    int32_t p[4], b[4], e[4];
+    int32_t sum_t = 0, sum_s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int g = g0 + k;
+      p[k] = 0;
+      b[k] = e[k] = 0;
+      if (g < nqt) {
+        const int h = g / nqt_head;
+        const int tr = (g - h * nqt_head) / refine_q;
+        b[k] = trow_ptr[h * ntr + tr];
+        e[k] = trow_ptr[h * ntr + tr + 1];
+        const int n = e[k] - b[k];
+        p[k] = (split > 0 && n > split) ? (n + split - 1) / split : 1;
+        sum_t += p[k];
+        sum_s += p[k] > 1 ? p[k] : 0;
+      }
+    }
+    int32_t tot_t, tot_s;
+    int32_t off_t = carry_t + block_scan(sum_t, lds, &tot_t);
+    int32_t off_s = carry_s + block_scan(sum_s, lds, &tot_s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int g = g0 + k;
+      if (g >= nqt) break;
+      const int h = g / nqt_head;
+      const int qt = g - h * nqt_head;
+      const int n = e[k] - b[k];
+      const int chunk = (n + p[k] - 1) / p[k];
+      parts[g] = p[k];
+      slot_base[g] = off_s;
+      for (int i = 0; i < p[k]; ++i) {
+        Task tk;
+        tk.head = h;
+        tk.qtile = qt;
+        tk.begin = min(e[k], b[k] + i * chunk);
+        tk.end = min(e[k], b[k] + (i + 1) * chunk);
+        tk.slot = p[k] > 1 ? off_s + i : -1;
+        tk.pad0 = tk.pad1 = tk.pad2 = 0;
+        tasks[off_t + i] = tk;
+      }
+      off_t += p[k];
+      off_s += p[k] > 1 ? p[k] : 0;
+    }
+    carry_t += tot_t;
+    carry_s += tot_s;
   }
+  if (t == 0) st->n_tasks = (unsigned long long)carry_t;
 }
 
 }  // namespace
 
-hipError_t launch_zero_stats(MaskStats* st, hipStream_t s) {
-  hipLaunchKernelGGL(k_zero_stats, dim3(1), dim3(64), 0, s, st);
-  return hipGetLastError();
-}
+int row_count_blocks(int32_t nrows) { return std::max(1, std::min((nrows + 3) / 4, 2048)); }
 
 hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_cnt,
-                            MaskStats* st, hipStream_t s) {
-  hipLaunchKernelGGL(k_row_count, dim3((nrows + 3) / 4), dim3(256), 0, s, mask, nrows, nkb,
-                     row_cnt, st);
+                            RowPartial* part, hipStream_t s) {
+  hipLaunchKernelGGL(k_row_count, dim3(row_count_blocks(nrows)), dim3(256), 0, s, mask, nrows, nkb,
+                     row_cnt, part);
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, unsigned long long* total,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, in, out, n, total);
+hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPartial* part,
+                       int32_t npart, MaskStats* st, hipStream_t s) {
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, in, out, n, part, npart, st);
   return hipGetLastError();
 }
 
@@ -270,21 +343,11 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
   return hipGetLastError();
 }
 
-hipError_t launch_task_count(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
-                             int32_t refine_q, int32_t split, int32_t* parts, int32_t* slots,
-                             hipStream_t s) {
-  const int n = H * nqt_head;
-  hipLaunchKernelGGL(k_task_count, dim3((n + 255) / 256), dim3(256), 0, s, trow_ptr, H, nqt_head,
-                     ntr, refine_q, split, parts, slots);
-  return hipGetLastError();
-}
-
-hipError_t launch_task_write(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
-                             int32_t refine_q, const int32_t* parts, const int32_t* task_off,
-                             const int32_t* slot_off, Task* tasks, hipStream_t s) {
-  const int n = H * nqt_head;
-  hipLaunchKernelGGL(k_task_write, dim3((n + 255) / 256), dim3(256), 0, s, trow_ptr, H, nqt_head,
-                     ntr, refine_q, parts, task_off, slot_off, tasks);
+hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
+                        int32_t refine_q, int32_t split, int32_t* parts, int32_t* slot_base,
+                        Task* tasks, MaskStats* st, hipStream_t s) {
+  hipLaunchKernelGGL(k_tasks, dim3(1), dim3(1024), 0, s, trow_ptr, H, nqt_head, ntr, refine_q, split,
+                     parts, slot_base, tasks, st);
   return hipGetLastError();
 }
 

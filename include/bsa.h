@@ -96,6 +96,7 @@ typedef struct {
   int64_t long_run_blocks; /* active blocks inside runs of length >= 2          */
   double density;       /* active / all logical blocks (section 5.1)            */
   double run_coverage;  /* long_run_blocks / active, 0 for an empty mask        */
+  double row_skew;      /* max_row_nnz * rows / active blocks (>= 1), 0 if empty */
   double host_select_us;   /* host time spent in regime lookup + ranking scan   */
 } bsa_plan_info;
 
@@ -130,7 +131,9 @@ bsa_status bsa_run(const bsa_plan* plan, const void* q, const void* k, const voi
 bsa_status bsa_run_timed(const bsa_plan* plan, const void* q, const void* k, const void* v,
                          void* o, void* stream, float* attn_ms, float* merge_ms);
 
-/* Release a plan (synchronizes the device first).  NULL is accepted. */
+/* Release a plan.  Waits for the plan's latest stream work (its creation or
+ * its most recent run) first; runs must not be in flight on other streams.
+ * NULL is accepted. */
 bsa_status bsa_plan_destroy(bsa_plan* plan);
 
 /* Copy the plan's scalar facts to *info (host). */
@@ -160,12 +163,20 @@ bsa_status bsa_catalog_get(int32_t id, bsa_catalog_entry* out);
  * no GPU.  *eligible receives 1 or 0. */
 bsa_status bsa_plan_eligible(int32_t id, const bsa_request* req, int32_t* eligible);
 
-/* Regime lookup and ranked fallback (section 5.2) on host-side features:
- * returns the selected catalog id, the regime index (-1 on a lookup miss, in
- * which case the key's base plan is the sole candidate) and BSA_OK, or
- * BSA_ERR_UNSUPPORTED when no candidate is eligible.  Touches no GPU. */
-bsa_status bsa_select(const bsa_request* req, double density, double run_coverage,
+/* Regime lookup and ranked fallback (section 5.2) on host-side features
+ * (density, run coverage, row skew -- see bsa_plan_info): returns the selected
+ * catalog id, the regime index (-1 on a lookup miss, in which case the key's
+ * base plan is the sole candidate) and BSA_OK, or BSA_ERR_UNSUPPORTED when no
+ * candidate is eligible.  Touches no GPU. */
+bsa_status bsa_select(const bsa_request* req, double density, double run_coverage, double row_skew,
                       int32_t* plan_id, int32_t* regime);
+
+/* Base plan of the request's key (paper section 5.1: the catalog plan that
+ * ends every ranking of the key and is the sole candidate on a lookup miss):
+ * Direct (T = B) with the default organization when the catalog has it, else
+ * the eligible entry with the smallest tile.  Host only.  *plan_id receives
+ * the catalog id, or -1 with BSA_ERR_UNSUPPORTED when no entry is eligible. */
+bsa_status bsa_base_plan(const bsa_request* req, int32_t* plan_id);
 
 /* Load a versioned plan table (text artifact) replacing the built-in one.
  * BSA_ERR_TABLE if unreadable, malformed, or built for another architecture

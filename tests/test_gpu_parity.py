@@ -95,3 +95,27 @@ def test_c2_medium():
         assert_close(out, ref, f"C2 plan {pid}")
         assert (out[7, :128].float() == 0).all() and (out[7, -128:].float() == 0).all()
         p.destroy()
+
+
+@pytest.mark.parametrize("block,N", [((64, 64), 1024), ((128, 32), 777), ((32, 128), 5000),
+                                     ((64, 64), 70)])
+def test_mask_state_matches_oracle(block, N):
+    """Block-CSR (bit-exact) and the scalar statistics of the shared mask
+    state against the oracle's definitions (density, run coverage)."""
+    from oracle import stats as ostats
+    H = 5
+    M, q, k, v = gen.random_case(H, N, 128, *block, p=0.35, seed=77 + N,
+                                 empty_rows={2: [0]}, dense_heads=(4,))
+    p, out = gpu_run(M, q, k, v, block)
+    info = p.info
+    rp, cols = p.export_csr()
+    Mb = np.asarray(M) != 0
+    nnz_row = Mb.reshape(-1, Mb.shape[-1]).sum(axis=1)
+    assert (np.diff(rp) == nnz_row).all() and rp[0] == 0
+    exp_cols = np.concatenate([np.nonzero(r)[0] for r in Mb.reshape(-1, Mb.shape[-1])])
+    assert (cols == exp_cols).all()
+    assert info["nnz_blocks"] == int(Mb.sum())
+    assert info["max_row_nnz"] == int(nnz_row.max())
+    assert info["density"] == pytest.approx(ostats.density(M), abs=1e-12)
+    assert info["run_coverage"] == pytest.approx(ostats.run_coverage(M), abs=1e-12)
+    p.destroy()

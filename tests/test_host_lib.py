@@ -34,14 +34,36 @@ def test_catalog_and_hash():
 
 def test_base_plan_direct_or_smallest_refined():
     cat = {e["id"]: e for e in bsa.catalog()}
-    pid, reg = bsa.select(8, 8192, 128, (128, 128), 0.3, 0.5)
-    e = cat[pid]
+    e = cat[bsa.base_plan(8, 8192, 128, (128, 128))]
     assert (e["tile_q"], e["tile_kv"]) == (128, 128)  # Direct when the catalog has T = B
-    pid, reg = bsa.select(24, 115200, 128, (32, 128), 0.1, 0.5)
-    e = cat[pid]
+    assert e["split"] == 1 and e["xcd_remap"] == 0  # default organization
+    e = cat[bsa.base_plan(24, 115200, 128, (32, 128))]
     assert e["tile_q"] * e["tile_kv"] == min(
         c["tile_q"] * c["tile_kv"] for c in cat.values()
         if bsa.eligible(c["id"], 24, 115200, 128, (32, 128)))
+
+
+def test_lookup_miss_returns_base_plan(tmp_path):
+    empty = tmp_path / "empty.txt"
+    empty.write_text(f"bsa-plan-table empty\narch gfx950\ncatalog {bsa.catalog_hash()}\n")
+    bsa.table_load(str(empty))
+    try:
+        for block in ((128, 128), (32, 128), (128, 32), (64, 64)):
+            pid, reg = bsa.select(8, 8192, 128, block, 0.3, 0.5)
+            assert reg == -1 and pid == bsa.base_plan(8, 8192, 128, block)
+    finally:
+        bsa.table_load(None)
+
+
+def test_builtin_table_is_versioned_and_covers_workload_keys():
+    assert bsa.table_version().startswith("v1")
+    for H, N, d, block, dens, rc, sk in ((8, 8192, 128, (128, 128), 0.31, 0.5, 3.2),
+                                         (40, 75600, 128, (64, 64), 0.13, 0.9, 1.3),
+                                         (24, 115200, 128, (128, 32), 0.17, 0.86, 1.7),
+                                         (24, 115200, 128, (32, 128), 0.2, 0.9, 1.5)):
+        pid, reg = bsa.select(H, N, d, block, dens, rc, sk)
+        assert reg >= 0, (block, N)
+        assert bsa.eligible(pid, H, N, d, block)
 
 
 def test_eligibility_rules():
@@ -72,7 +94,7 @@ def test_table_load_rejects_bad_tables(tmp_path):
     good = tmp_path / "g.txt"
     name = bsa.catalog()[3]["name"]
     good.write_text(f"bsa-plan-table test1\narch gfx950\ncatalog {bsa.catalog_hash()}\n"
-                    f"bounds density 0.2\nregime 128 128 128 * * 1 * : {name}\n")
+                    f"bounds density 0.2\nregime 128 128 128 * * 1 * * : {name}\n")
     bsa.table_load(str(good))
     try:
         assert bsa.table_version() == "test1"
