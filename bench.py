@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--force-split", type=int, default=-1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (5 times): the "
+                         "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -118,6 +121,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 5}), flush=True)
+        return
 
     import dynamic_block_sparse_bsa_amd as bsa
     from workloads import gen

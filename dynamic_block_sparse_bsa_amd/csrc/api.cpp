@@ -449,8 +449,8 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split,
                        (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr, dst, s));
   if (shape.slots_upper > 0) HIP_TRY(pool_alloc(p->dev, (size_t)shape.ws_bytes, &p->ws));
-  p->grid = chosen->xcd_remap ? cdiv(shape.tasks_upper, 8) * 8 : shape.tasks_upper;
-  if (p->grid < 1) p->grid = chosen->xcd_remap ? 8 : 1;
+  const int64_t gran = chosen->xcd_remap > 0 ? 8 * (int64_t)chosen->xcd_remap : 1;
+  p->grid = cdiv(std::max<int64_t>(shape.tasks_upper, 1), gran) * gran;
   if (p->grid >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many tasks");
   HIP_TRY(hipGetLastError());
 

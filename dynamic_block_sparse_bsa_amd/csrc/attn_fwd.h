@@ -158,9 +158,14 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
 
   // ---- task -------------------------------------------------------------
   int bid = blockIdx.x;
-  if (a.xcd_remap) {
-    const int per = a.grid >> 3;
-    bid = (bid & 7) * per + (bid >> 3);
+  if (a.xcd_remap > 0) {
+    // Workgroups are dealt to the 8 XCDs round-robin by id.  Remap so that
+    // each XCD receives runs of xcd_remap consecutive tasks (neighbouring
+    // query tiles of a head, which share K/V tiles in that XCD's L2), while
+    // all XCDs still advance through the task list together.
+    const int C = a.xcd_remap;
+    const int s = bid >> 3;
+    bid = (s / C) * (8 * C) + (bid & 7) * C + (s % C);
   }
   if ((unsigned long long)bid >= *a.n_tasks) return;
   const Task task = a.tasks[bid];

@@ -57,8 +57,8 @@ struct AttnArgs {
   int32_t coarsen_kv;     // logical K/V blocks per tile (membership decode)
   int32_t bq;             // B_Q (membership decode when coarsen_q > 1)
   int32_t coarsen_q;
-  int32_t xcd_remap;      // 1: group consecutive tasks on one XCD
-  int32_t grid;           // workgroups launched (multiple of 8 when remapped)
+  int32_t xcd_remap;      // > 0: runs of this many consecutive tasks per XCD
+  int32_t grid;           // workgroups launched (multiple of 8 * xcd_remap when remapped)
   float scale_log2;       // log2(e) / sqrt(d)
 };
 

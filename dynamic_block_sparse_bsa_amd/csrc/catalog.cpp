@@ -15,6 +15,8 @@ namespace {
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+constexpr int kXcdRun = 16;  // tasks per XCD run of the "_xcd" organization
+
 std::vector<CatalogEntry> build_catalog() {
   // kernel tile shapes instantiated for gfx950 (attn_kernels.hip), per head dim
   struct Shape {
@@ -26,8 +28,9 @@ std::vector<CatalogEntry> build_catalog() {
                                  {256, 64, 64}};
   std::vector<CatalogEntry> c;
   for (const Shape& s : shapes) {
-    // organizations: split-K balance rule; no split; split-K + per-XCD grouping
-    const int orgs[][2] = {{1, 0}, {0, 0}, {1, 1}};
+    // organizations: split-K balance rule; no split; split-K + runs of
+    // kXcdRun consecutive tasks per XCD
+    const int orgs[][2] = {{1, 0}, {0, 0}, {1, kXcdRun}};
     for (auto& o : orgs) {
       CatalogEntry e;
       e.id = (int)c.size();

@@ -3,13 +3,23 @@
 // are rescaled to their common maximum, summed and normalized.  Running
 // maxima are in log2 units (scores times log2(e)/sqrt(d)), so the weights are
 // exp2(m_p - m*).  A row whose partitions are all empty (l = 0) outputs zeros.
-// HBM-bound: each partial element is read once, each output written once.
+//
+// One workgroup per (split query tile, 32 output columns), so even a few
+// split tiles spread over many CUs.  The per-row weights w_p / sum_p w_p l_p
+// are computed once per workgroup (one thread per row) into LDS; the threads
+// then stream the partial accumulators, four output columns per thread item,
+// reading [slot][d][T_Q] rows contiguously.  HBM-bound: each partial element
+// is read once and each output element written once.
 #include "bsa_internal.h"
 
 namespace bsa {
 namespace {
 
+constexpr int kMaxParts = 32;   // partitions whose weights are held in LDS
+constexpr int kMaxTq = 256;
+
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
+  __shared__ float wgt[kMaxParts][kMaxTq];
   const int g = blockIdx.x;
   const int parts = a.parts[g];
   if (parts <= 1) return;
@@ -18,42 +28,70 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   const int sb = a.slot_base[g];
   const int TQ = a.tq;
   const int D = a.d;
-  const int nch = D / 8;  // 8 output values per thread item
-  for (int item = threadIdx.x; item < TQ * nch; item += 256) {
-    const int r = item % TQ;
-    const int dc = item / TQ;
-    const int row = qt * TQ + r;
-    if (row >= a.N) continue;
-    float mstar = -INFINITY;
+  const int t = threadIdx.x;
+  // (1) per-row common maximum and normalizer; weights of the first kMaxParts
+  // partitions go to LDS, further ones are recomputed while streaming
+  float mstar = -INFINITY, inv = 0.0f;
+  if (t < TQ) {
     for (int p = 0; p < parts; ++p) {
-      const size_t s = (size_t)(sb + p);
-      if (a.ws_l[s * TQ + r] > 0.0f) mstar = fmaxf(mstar, a.ws_m[s * TQ + r]);
+      const size_t s = (size_t)(sb + p) * TQ + t;
+      if (a.ws_l[s] > 0.0f) mstar = fmaxf(mstar, a.ws_m[s]);
     }
-    float num[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float den = 0.0f;
     for (int p = 0; p < parts; ++p) {
-      const size_t s = (size_t)(sb + p);
-      const float l = a.ws_l[s * TQ + r];
-      if (!(l > 0.0f)) continue;
-      const float wgt = __builtin_amdgcn_exp2f(a.ws_m[s * TQ + r] - mstar);
-      den += wgt * l;
-      const float* o = a.ws_o + s * (size_t)D * TQ + (size_t)(dc * 8) * TQ + r;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) num[i] += wgt * o[(size_t)i * TQ];
+      const size_t s = (size_t)(sb + p) * TQ + t;
+      const float l = a.ws_l[s];
+      const float w = l > 0.0f ? __builtin_amdgcn_exp2f(a.ws_m[s] - mstar) : 0.0f;
+      den += w * l;
+      if (p < kMaxParts) wgt[p][t] = w;
     }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    __bf16 outv[8];
+    inv = den > 0.0f ? 1.0f / den : 0.0f;
+    for (int p = 0; p < min(parts, kMaxParts); ++p) wgt[p][t] *= inv;
+  }
+  __syncthreads();
+  // (2) out[r][c..c+3] = sum_p wgt[p][r] * O_p[c..c+3][r], c in this
+  // workgroup's 32 columns
+  const int nitems = TQ * 8;
+  for (int item = t; item < nitems; item += 256) {
+    const int r = item % TQ;
+    const int c = blockIdx.y * 32 + (item / TQ) * 4;
+    const int row = qt * TQ + r;
+    if (row >= a.N) continue;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p = 0; p < parts; ++p) {
+      float w;
+      if (p < kMaxParts) {
+        w = wgt[p][r];
+      } else {  // recompute (rare: more than kMaxParts partitions)
+        float ms = -INFINITY, den = 0.0f;
+        for (int q = 0; q < parts; ++q) {
+          const size_t s = (size_t)(sb + q) * TQ + r;
+          if (a.ws_l[s] > 0.0f) ms = fmaxf(ms, a.ws_m[s]);
+        }
+        for (int q = 0; q < parts; ++q) {
+          const size_t s = (size_t)(sb + q) * TQ + r;
+          if (a.ws_l[s] > 0.0f) den += __builtin_amdgcn_exp2f(a.ws_m[s] - ms) * a.ws_l[s];
+        }
+        const size_t s = (size_t)(sb + p) * TQ + r;
+        w = (a.ws_l[s] > 0.0f && den > 0.0f) ? __builtin_amdgcn_exp2f(a.ws_m[s] - ms) / den : 0.0f;
+      }
+      const float* o = a.ws_o + (size_t)(sb + p) * D * TQ + (size_t)c * TQ + r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) outv[i] = (__bf16)(num[i] * inv);
-    __bf16* op = a.o + ((size_t)h * a.N + row) * D + dc * 8;
-    *reinterpret_cast<uint4*>(op) = *reinterpret_cast<const uint4*>(outv);
+      for (int i = 0; i < 4; ++i) acc[i] += w * o[(size_t)i * TQ];
+    }
+    __bf16 ov[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc[i];
+    *reinterpret_cast<uint2*>(a.o + ((size_t)h * a.N + row) * D + c) = *reinterpret_cast<const uint2*>(ov);
   }
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s) {
-  hipLaunchKernelGGL(k_merge, dim3(n_qtiles), dim3(256), 0, s, a);
+  if (a.tq > kMaxTq) return hipErrorInvalidValue;
+  if (a.d % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_merge, dim3(n_qtiles, a.d / 32), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

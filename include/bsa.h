@@ -105,7 +105,7 @@ typedef struct {
   int32_t id;
   int32_t tile_q, tile_kv, d;
   int32_t split;        /* 0 = never split, 1 = balance rule                    */
-  int32_t xcd_remap;    /* 1 = tasks grouped per XCD                             */
+  int32_t xcd_remap;    /* > 0: runs of this many consecutive tasks per XCD      */
   char name[48];
 } bsa_catalog_entry;
 
