@@ -146,7 +146,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int TQ, int TKV, int D>
-__global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(TQ * 2) __attribute__((amdgpu_waves_per_eu(TKV == 32 && D == 128 ? 3 : 1))) void attn_fwd_kernel(const AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using S = AttnShape<TQ, TKV, D>;
   constexpr int STAGE = S::KBYTES + S::VBYTES;
@@ -180,14 +180,17 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   const int qrow = task.qtile * TQ + w * 32 + n;
 
   // ---- Q fragment: B operand of S^T = K Q^T, resident for the task -------
+  // Q is pre-multiplied by log2(e)/sqrt(d) (and rounded to bf16), so the MFMA
+  // yields scores in log2 units.
   bf16x8 qf[S::DK];
   {
     const bool ok = qrow < N;
     const __bf16* qp = a.q + head_off + (size_t)(ok ? qrow : 0) * D + 8 * hh;
 #pragma unroll
     for (int c = 0; c < S::DK; ++c) {
-      qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
-      if (!ok) qf[c] = bf16x8{};
+      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)(ok ? (float)raw[e] * a.scale_log2 : 0.0f);
     }
   }
 
@@ -199,9 +202,14 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   // ---- online-softmax state (lane-local; l is a half-sum over this lane's keys)
   // m_run is a reference maximum in log2 units; it is raised only when a score
   // exceeds it by more than 8, so P stays <= 2^8 and the O rescale is rare.
+  // The QK^T accumulator starts from cm = -m_run (0 while m_run = -inf), so
+  // the MFMA emits exponents ready for v_exp_f32: no per-score subtract.
   float m_run = -INFINITY;
   float l_run = 0.0f;
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+  f32x16 cm;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cm[v] = 0.0f;
   f32x16 acc[S::DB];
 #pragma unroll
   for (int b = 0; b < S::DB; ++b) acc[b] = f32x16{};
@@ -254,16 +262,27 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   }
   const char* const kh = reinterpret_cast<const char*>(a.k + head_off);
   const char* const vh = reinterpret_cast<const char*>(a.v + head_off);
+  // raw buffer descriptors over this head's K and V (bytes [0, N*D*2))
+  constexpr int kRsrcWord3 = 0x00020000;
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kh), (short)0, N * (D * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vh), (short)0, N * (D * 2), kRsrcWord3);
   auto issue = [&](int kv0, int buf) {
     unsigned char* kb = smem + buf * STAGE + w * 1024;
     unsigned char* vb = kb + S::KBYTES;
     const char* kt = kh + (size_t)kv0 * (D * 2);
     const char* vt = vh + (size_t)kv0 * (D * 2);
     if (kv0 + TKV <= N) {
+      // buffer loads: head base in the descriptor, tile offset in an SGPR,
+      // per-lane offset in a VGPR fixed for the task -- no address VALU work
+      const int soff = kv0 * (D * 2);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        __builtin_amdgcn_global_load_lds(kt + goff[i], (lds_void*)(kb + i * S::WAVES * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + goff[i], (lds_void*)(vb + i * S::WAVES * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(kb + i * S::WAVES * 1024), 16, goff[i],
+                                                 soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)(vb + i * S::WAVES * 1024), 16, goff[i],
+                                                 soff, 0, 0);
       }
     } else {
       const int last = (N - 1 - kv0) * (D * 2);  // offset of row N-1 within the tile
@@ -356,11 +375,10 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
       f32x16 s[S::NST];
 #pragma unroll
       for (int st = 0; st < S::NST; ++st) {
-        s[st] = f32x16{};
 #pragma unroll
         for (int c = 0; c < S::DK; ++c) {
           const bf16x8 kf = *(const lds_bf16x8*)(kl + st * 32 * (D * 2) + (kbase ^ (c << 5)));
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[st], 0, 0, 0);
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? cm : s[st], 0, 0, 0);
         }
       }
       // ---- masking: inactive logical blocks of the tile, keys >= N ---------
@@ -384,31 +402,37 @@ __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
             if (st * 32 + 16 * (v >> 3) + (v & 7) >= lim) s[st][v] = -INFINITY;
       }
       // ---- online softmax (exp2 domain, lazy rescale) ---------------------
+      // Scores are s - m_use; the reference is raised when one exceeds it by
+      // more than 8 (or at the row's first active key).
       float mx = -INFINITY;
 #pragma unroll
       for (int st = 0; st < S::NST; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
-      mx = fmaxf(mx, other_half(mx)) * a.scale_log2;
-      const bool grow = mx > m_run + 8.0f;
+      mx = fmaxf(mx, other_half(mx));
+      const bool first = (m_run == -INFINITY) && (mx != -INFINITY);
+      const bool grow = first || (mx > 8.0f);
       if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        const float delta = grow ? mx : 0.0f;
+        const float alpha = (grow && !first) ? __builtin_amdgcn_exp2f(-delta) : 1.0f;
+        if (grow) m_run = (first ? 0.0f : m_run) + delta;
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < S::DB; ++b) acc[b] *= alpha;
+#pragma unroll
+        for (int st = 0; st < S::NST; ++st)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[st][v] -= delta;
+        const float neg = (m_run == -INFINITY) ? 0.0f : -m_run;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cm[v] = neg;
       }
-      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
 
       bf16x8 pf[S::NST][2];
 #pragma unroll
       for (int st = 0; st < S::NST; ++st)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[st][v], a.scale_log2, -m_use));
-          pf[st][v >> 3][v & 7] = (__bf16)p;
-        }
+        for (int v = 0; v < 16; ++v) pf[st][v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(s[st][v]);
       // l accumulates the bf16-rounded probabilities that enter the PV
       // product, two per v_dot2 against (1, 1).
 #pragma unroll
