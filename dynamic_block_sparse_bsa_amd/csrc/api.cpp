@@ -114,11 +114,17 @@ void pool_release(DevBuf* b) {
   b->ptr = nullptr;
 }
 
-// pinned host staging for the statistics transfer, one per thread
+constexpr size_t kEarlyCompactBytes = size_t(16) << 20;
+
+// Fine-grained (coherent) pinned host memory, one per thread, that the mask
+// state kernels write the statistics into directly: the single device-to-host
+// crossing of the request path needs no separate copy.
 MaskStats* pinned_stats() {
   thread_local MaskStats* p = nullptr;
   if (!p) {
-    if (hipHostMalloc((void**)&p, sizeof(MaskStats), hipHostMallocDefault) != hipSuccess) p = nullptr;
+    if (hipHostMalloc((void**)&p, sizeof(MaskStats), hipHostMallocCoherent | hipHostMallocPortable) !=
+        hipSuccess)
+      p = nullptr;
   }
   return p;
 }
@@ -359,21 +365,29 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   p->nkb = (int)cdiv(r.N, r.block_kv);
   const int nrows = r.H * p->nqb;
 
-  // ---- shared mask state: counts, offsets, statistics -------------------------
-  HIP_TRY(pool_alloc(p->dev, sizeof(MaskStats), &p->stats_dev));
-  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
-  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nrows + 1), &p->row_ptr));
-  const int npart = row_count_blocks(nrows);
-  HIP_TRY(pool_alloc(p->dev, sizeof(RowPartial) * (size_t)npart, &p->row_part));
-  MaskStats* dst = (MaskStats*)p->stats_dev.ptr;
-  RowPartial* part = (RowPartial*)p->row_part.ptr;
-  HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, part, s));
-  HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, s));
+  // ---- shared mask state: counts, offsets, columns, statistics ---------------
   MaskStats* host = pinned_stats();
   if (!host) return fail(BSA_ERR_NO_MEMORY, "pinned host allocation failed");
-  HIP_TRY(hipMemcpyAsync(host, dst, sizeof(MaskStats), hipMemcpyDeviceToHost, s));
+  HIP_TRY(pool_alloc(p->dev, sizeof(MaskStats), &p->stats_dev));
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nrows + 1), &p->row_ptr));
+  MaskStats* dst = (MaskStats*)p->stats_dev.ptr;
+  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
+  const int npart = row_count_blocks(nrows);
+  HIP_TRY(pool_alloc(p->dev, sizeof(RowPartial) * (size_t)npart, &p->row_part));
+  RowPartial* part = (RowPartial*)p->row_part.ptr;
+  HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, part, s));
+  HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, host, s));
+  // When a column array sized for every block is modest, the compaction is
+  // queued before the statistics synchronization, so it overlaps the host's
+  // wait and plan selection.
+  const size_t cols_bound = sizeof(int32_t) * (size_t)nrows * (size_t)p->nkb;
+  const bool early_compact = cols_bound <= kEarlyCompactBytes;
+  if (early_compact) {
+    HIP_TRY(pool_alloc(p->dev, cols_bound, &p->cols));
+    HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
+  }
   HIP_TRY(hipStreamSynchronize(s));
-  p->stats = *host;
+  std::memcpy(&p->stats, host, sizeof(MaskStats));
   const double total_blocks = (double)r.H * p->nqb * p->nkb;
   const double density = p->stats.nnz / total_blocks;
   const double runcov = p->stats.nnz ? (double)p->stats.long_run / (double)p->stats.nnz : 0.0;
@@ -408,10 +422,12 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   p->entry = chosen;
   p->shape = shape;
 
-  // ---- block-CSR columns ------------------------------------------------------
+  // ---- block-CSR columns (unless queued before the synchronization) ----------
   const size_t nnz = (size_t)p->stats.nnz;
-  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->cols));
-  HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
+  if (!early_compact) {
+    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->cols));
+    HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
+  }
 
   // ---- launch preparation: tile list of the selected mapping -------------------
   const int cq = shape.mq.coarsen, ckv = shape.mk.coarsen;
@@ -427,7 +443,7 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
                            ntc, (int32_t*)p->trow_cnt.ptr, nullptr, nullptr, nullptr, s));
     HIP_TRY(launch_scan((int32_t*)p->trow_cnt.ptr, (int32_t*)p->trow_ptr_buf.ptr, ntrows, nullptr, 0, nullptr,
-                        s));
+                        nullptr, s));
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
                            ntc, nullptr, (int32_t*)p->trow_ptr_buf.ptr, (int32_t*)p->tcol_buf.ptr,
                            (uint32_t*)p->tbits_buf.ptr, s));

@@ -81,9 +81,10 @@ using AttnLauncher = hipError_t (*)(const AttnArgs&, int grid, hipStream_t);
 int row_count_blocks(int32_t nrows);  // workgroups (= partials) of the row-count kernel
 hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_cnt,
                             RowPartial* part, hipStream_t s);
-// Exclusive scan; with st non-null also completes the mask statistics.
+// Exclusive scan; with st non-null also completes the mask statistics (and
+// copies them to host_st, fine-grained host memory, when non-null).
 hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPartial* part,
-                       int32_t npart, MaskStats* st, hipStream_t s);
+                       int32_t npart, MaskStats* st, MaskStats* host_st, hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
                           int32_t* cols, hipStream_t s);
 hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,

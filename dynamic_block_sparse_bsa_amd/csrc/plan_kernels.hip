@@ -102,7 +102,7 @@ __device__ int32_t block_scan(int32_t v, int32_t* lds, int32_t* tot) {
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
                                                int32_t* __restrict__ out, int32_t n,
                                                const RowPartial* __restrict__ part, int32_t npart,
-                                               MaskStats* st) {
+                                               MaskStats* st, MaskStats* host_st) {
   __shared__ int32_t lds[1024];
   const int t = threadIdx.x;
   int32_t carry = 0;
@@ -145,11 +145,14 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
       __syncthreads();
     }
     if (t == 0) {
-      st->nnz = (unsigned long long)carry;
-      st->long_run = s_long[0];
-      st->max_row_nnz = s_max[0];
-      st->empty_rows = s_empty[0];
-      st->n_tasks = 0;
+      MaskStats r;
+      r.nnz = (unsigned long long)carry;
+      r.long_run = s_long[0];
+      r.max_row_nnz = s_max[0];
+      r.empty_rows = s_empty[0];
+      r.n_tasks = 0;
+      *st = r;
+      if (host_st) *host_st = r;  // fine-grained host memory: no copy needed
     }
   }
 }
@@ -320,8 +323,8 @@ hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int
 }
 
 hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPartial* part,
-                       int32_t npart, MaskStats* st, hipStream_t s) {
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, in, out, n, part, npart, st);
+                       int32_t npart, MaskStats* st, MaskStats* host_st, hipStream_t s) {
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, in, out, n, part, npart, st, host_st);
   return hipGetLastError();
 }
 
