@@ -146,7 +146,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int TQ, int TKV, int D>
-__global__ __launch_bounds__(TQ * 2) __attribute__((amdgpu_waves_per_eu(TKV == 32 && D == 128 ? 3 : 1))) void attn_fwd_kernel(const AttnArgs a) {
+__device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using S = AttnShape<TQ, TKV, D>;
   constexpr int STAGE = S::KBYTES + S::VBYTES;
@@ -538,9 +538,27 @@ __global__ __launch_bounds__(TQ * 2) __attribute__((amdgpu_waves_per_eu(TKV == 3
 #endif
 }
 
+// Entry points: the generic kernel, and the one for 32-key tiles at d = 128
+// with at most 128 queries, whose registers are capped at 168 so three waves
+// fit a SIMD (the lower-occupancy schedule measured slower).
+template <int TQ, int TKV, int D>
+__global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
+  attn_fwd_body<TQ, TKV, D>(a);
+}
+template <int TQ, int TKV, int D>
+__global__ __launch_bounds__(TQ * 2) __attribute__((amdgpu_waves_per_eu(3)))
+__attribute__((amdgpu_num_vgpr(168))) void attn_fwd_kernel_w3(const AttnArgs a) {
+  attn_fwd_body<TQ, TKV, D>(a);
+}
+template <int TQ, int TKV, int D>
+constexpr bool use_w3() { return TKV == 32 && D == 128 && TQ == 128; }
+
 template <int TQ, int TKV, int D>
 hipError_t launch_attn(const AttnArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<TQ, TKV, D>), dim3(grid), dim3(TQ * 2), 0, s, a);
+  if constexpr (use_w3<TQ, TKV, D>())
+    hipLaunchKernelGGL((attn_fwd_kernel_w3<TQ, TKV, D>), dim3(grid), dim3(TQ * 2), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<TQ, TKV, D>), dim3(grid), dim3(TQ * 2), 0, s, a);
   return hipGetLastError();
 }
 

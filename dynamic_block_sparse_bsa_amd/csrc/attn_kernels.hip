@@ -24,15 +24,20 @@ AttnLauncher attn_launcher(int tq, int tkv, int d) {
   return nullptr;
 }
 
-int attn_wg_per_cu(int tq, int tkv, int d) {
+template <int TQ, int TKV, int D>
+static int wg_per_cu() {
   int n = 0;
-#define BSA_CASE(TQ_, TKV_, D_)                                                               \
-  if (tq == TQ_ && tkv == TKV_ && d == D_) {                                                  \
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel<TQ_, TKV_, D_>,      \
-                                                     TQ_ * 2, 0) != hipSuccess)               \
-      n = 0;                                                                                  \
-    return n;                                                                                 \
-  }
+  hipError_t e;
+  if constexpr (use_w3<TQ, TKV, D>())
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel_w3<TQ, TKV, D>, TQ * 2, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel<TQ, TKV, D>, TQ * 2, 0);
+  return e == hipSuccess ? n : 0;
+}
+
+int attn_wg_per_cu(int tq, int tkv, int d) {
+#define BSA_CASE(TQ_, TKV_, D_) \
+  if (tq == TQ_ && tkv == TKV_ && d == D_) return wg_per_cu<TQ_, TKV_, D_>();
   BSA_CASE(64, 32, 128)
   BSA_CASE(64, 64, 128)
   BSA_CASE(128, 32, 128)
