@@ -1,0 +1,95 @@
+"""CPU checks of the offline plan-table compiler (paper section 5.1): regime
+partition by request key and feature buckets, geometric-mean ranking over the
+plans valid on every case of a regime, the base plan at the end of every
+ranking, and a versioned artifact the library accepts.  No GPU: the records
+are synthetic latency tables."""
+
+import math
+
+import pytest
+
+import dynamic_block_sparse_bsa_amd as bsa
+from dynamic_block_sparse_bsa_amd import profile_table as pt
+
+
+def _ids(block, d=128, H=8, N=8192):
+    return [e["id"] for e in bsa.catalog() if bsa.eligible(e["id"], H, N, d, block)]
+
+
+def _rec(block, N, density, runcov, skew, lat, H=8, d=128):
+    return dict(block=block, d=d, H=H, N=N, family="iid", rho=density, seed=0, density=density,
+                run_coverage=runcov, row_skew=skew, latency=lat)
+
+
+def test_bucket_bounds():
+    assert pt.bucket([0.1, 0.2], 0.05) == 0
+    assert pt.bucket([0.1, 0.2], 0.1) == 1  # bucket k holds bounds[k-1] <= x < bounds[k]
+    assert pt.bucket([0.1, 0.2], 0.5) == 2
+    assert pt.bucket([], 3.0) == 0
+
+
+def test_geometric_mean_ranking_and_validity(tmp_path):
+    ids = _ids((128, 128))
+    a, b, c = ids[0], ids[3], ids[6]
+    # plan a: GM sqrt(1*4) = 2; plan b: GM sqrt(2*2) = 2.0 + tie-break by id; plan c: 1.5 but
+    # invalid on the second case (missing) -> excluded from the regime's ranking
+    recs = [_rec((128, 128), 8192, 0.3, 0.6, 1.2, {a: 1.0, b: 2.0, c: 1.5}),
+            _rec((128, 128), 8192, 0.31, 0.7, 1.3, {a: 4.0, b: 2.1})]
+    text = pt.compile_table(recs, "vtest")
+    lines = [ln for ln in text.splitlines() if ln.startswith("regime")]
+    assert len(lines) == 1  # both cases fall in one regime
+    names = {e["id"]: e["name"] for e in bsa.catalog()}
+    ranking = lines[0].split(" : ")[1].split()
+    gm_a, gm_b = math.sqrt(1.0 * 4.0), math.sqrt(2.0 * 2.1)
+    assert gm_a < gm_b
+    assert ranking[0] == names[a] and ranking[1] == names[b]
+    assert names[c] not in ranking[:2]
+    assert ranking[-1] == names[bsa.base_plan(8, 8192, 128, (128, 128))]
+    # regime fields: key, H wildcard, buckets of N, density, run coverage, row skew
+    f = lines[0].split(" : ")[0].split()
+    assert f[1:4] == ["128", "128", "128"] and f[4] == "*"
+    assert f[5:] == [str(pt.bucket(pt.BOUNDS["N"], 8192)), str(pt.bucket(pt.BOUNDS["density"], 0.3)),
+                     str(pt.bucket(pt.BOUNDS["run_coverage"], 0.6)),
+                     str(pt.bucket(pt.BOUNDS["row_skew"], 1.2))]
+    # the artifact loads and the lookup returns the regime's top plan
+    path = tmp_path / "t.txt"
+    path.write_text(text)
+    bsa.table_load(str(path))
+    try:
+        assert bsa.table_version() == "vtest"
+        pid, reg = bsa.select(8, 8192, 128, (128, 128), 0.3, 0.6, 1.2)
+        assert reg == 0 and pid == a
+        pid, reg = bsa.select(8, 8192, 128, (128, 128), 0.05, 0.6, 1.2)  # other density bucket
+        assert reg == -1 and pid == bsa.base_plan(8, 8192, 128, (128, 128))
+    finally:
+        bsa.table_load(None)
+
+
+def test_cases_split_by_key_and_buckets():
+    i128, i64 = _ids((128, 128)), _ids((64, 64))
+    recs = [_rec((128, 128), 8192, 0.3, 0.6, 1.0, {i128[0]: 1.0}),
+            _rec((128, 128), 8192, 0.3, 0.6, 3.0, {i128[1]: 1.0}),   # row-skew bucket differs
+            _rec((128, 128), 100000, 0.3, 0.6, 1.0, {i128[2]: 1.0}),  # N bucket differs
+            _rec((64, 64), 8192, 0.3, 0.6, 1.0, {i64[0]: 1.0})]       # key differs
+    text = pt.compile_table(recs, "v2")
+    assert sum(ln.startswith("regime") for ln in text.splitlines()) == 4
+
+
+def test_corpus_seeds_disjoint_from_workloads():
+    cases = pt.corpus()
+    seeds = {c["seed"] for c in cases}
+    assert len(seeds) == len(cases) and min(seeds) >= 900000
+    # the benchmark workloads draw from 1000*c (+0..3) and 5000 + 10*r (+0..3)
+    assert not seeds & ({1000 * c + k for c in range(1, 6) for k in range(4)} |
+                        {5000 + 10 * r + k for r in range(50) for k in range(4)})
+    assert {c["family"] for c in cases} == {"clustered", "window", "iid", "iid_mixed"}
+    assert all(bsa.base_plan(c["H"], c["N"], c["d"], c["block"]) >= 0 for c in cases)
+
+
+@pytest.mark.parametrize("fam", ["clustered", "window", "iid", "iid_mixed"])
+def test_corpus_masks_have_requested_shape(fam):
+    block = (64, 64)
+    c = dict(block=block, d=128, H=4, N=4096, family=fam, rho=0.2, seed=900001)
+    M = pt.make_mask(c)
+    assert M.shape == (4, 64, 64) and M.dtype.name == "uint8"
+    assert 0.02 < (M != 0).mean() < 0.6
