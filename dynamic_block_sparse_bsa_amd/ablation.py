@@ -1,0 +1,192 @@
+"""Selection-quality ablation on a held-out synthetic corpus (run on the MI355X).
+
+    python -m dynamic_block_sparse_bsa_amd.ablation [--out PATH] [--quick]
+
+Tessera paper, section 7.4 "Plan Selection Preserves Gains at Low Cost" and
+its Table 7 compare three ways to serve a request:
+  A0  Direct mapping (T = B) with the base task organization,
+  A1  exhaustive online search: prepare and probe every eligible catalog
+      plan, then execute the fastest,
+  A2  the plan table: regime lookup, ranked fallback, prepare only the
+      selected plan.
+Reported per variant, over the cases: geometric-mean kernel speedup over A0,
+selection regret of A2 against the fastest eligible plan (GM, P95, max and
+the share of cases within 3% of it), wins/ties/losses of A2 against A0 with
+the paper's 3% tie band, and complete-request latencies for a cold request
+(A1 includes every probe) and for warm exact repeats (the prepared plan is
+reused, so repeats cost one run).
+
+The held-out cases use the profiler's generators with seeds from 950000,
+disjoint from both the profiling corpus (900000...) and the benchmark.
+"""
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+TIE = 0.03
+
+
+def heldout(quick=False):
+    from dynamic_block_sparse_bsa_amd import profile_table as pt
+    cases = []
+    seed = 950000
+    keys = [((64, 64), 128), ((128, 128), 128), ((128, 32), 128), ((32, 128), 128)]
+    sizes = [(8, 8192), (4, 32768), (4, 75600)] if not quick else [(4, 8192)]
+    dens = [0.05, 0.12, 0.22, 0.35] if not quick else [0.15]
+    fams = ["clustered", "iid_mixed", "window", "iid"]
+    for block, d in keys:
+        for H, N in sizes:
+            for i, rho in enumerate(dens):
+                fam = fams[(i + H) % 4]
+                if fam == "window" and block[0] != block[1]:
+                    fam = "clustered"
+                cases.append(dict(block=block, d=d, H=H, N=N, family=fam, rho=rho, seed=seed))
+                seed += 1
+    return cases, pt.make_mask
+
+
+def _gm(xs):
+    return math.exp(sum(math.log(x) for x in xs) / len(xs)) if xs else float("nan")
+
+
+def run(cases, make_mask, reps=5, warmup=2, log=print):
+    import torch
+
+    import dynamic_block_sparse_bsa_amd as bsa
+    from workloads import gen
+    dev = torch.device("cuda")
+    cat = {e["id"]: e for e in bsa.catalog()}
+    rows = []
+
+    def request(Md, block, H, N, d, q, k, v, out, force=-1):
+        """one complete request: plan + run + sync (+ release); ms"""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        p = bsa.plan(Md, block, H, N, d, force_plan=force)
+        bsa.run(p, q, k, v, out)
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) * 1e3
+        return p, t
+
+    def kernel_ms(p, q, k, v, out):
+        ts = []
+        for i in range(warmup + reps):
+            _, a, m = bsa.run_timed(p, q, k, v, out)
+            if i >= warmup:
+                ts.append(a + m)
+        return statistics.median(ts)
+
+    def warm_ms(p, q, k, v, out):
+        ts = []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            bsa.run(p, q, k, v, out)
+            torch.cuda.synchronize()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return statistics.median(ts)
+
+    for ci, c in enumerate(cases):
+        H, N, d, block = c["H"], c["N"], c["d"], c["block"]
+        M = make_mask(c)
+        q, k, v = (t.to(dev) for t in gen.qkv(H, N, d, (c["seed"] + 1, c["seed"] + 2, c["seed"] + 3)))
+        Md = torch.from_numpy(M).to(dev)
+        out = torch.empty_like(q)
+        eligible = [i for i in cat if bsa.eligible(i, H, N, d, block)]
+        base = bsa.base_plan(H, N, d, block)
+        # warm the process-wide caches once per case (first use of a kernel)
+        for pid in eligible:
+            bsa.plan(Md, block, H, N, d, force_plan=pid).destroy()
+        # A1: cold exhaustive search = prepare and probe every eligible plan, run the best
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        probe = {}
+        for pid in eligible:
+            p = bsa.plan(Md, block, H, N, d, force_plan=pid)
+            _, a, m = bsa.run_timed(p, q, k, v, out)
+            probe[pid] = a + m
+            p.destroy()
+        best_probe = min(probe, key=probe.get)
+        p = bsa.plan(Md, block, H, N, d, force_plan=best_probe)
+        bsa.run(p, q, k, v, out)
+        torch.cuda.synchronize()
+        a1_cold = (time.perf_counter() - t0) * 1e3
+        p.destroy()
+        # kernel latency of every eligible plan (the fastest is the oracle choice)
+        lat = {}
+        for pid in eligible:
+            p = bsa.plan(Md, block, H, N, d, force_plan=pid)
+            lat[pid] = kernel_ms(p, q, k, v, out)
+            p.destroy()
+        fastest = min(lat, key=lat.get)
+        # A0 and A2 complete requests (cold = plan + run), warm repeats, selected ids
+        p0, a0_cold = request(Md, block, H, N, d, q, k, v, out, force=base)
+        a0_warm = warm_ms(p0, q, k, v, out)
+        p0.destroy()
+        p2, a2_cold = request(Md, block, H, N, d, q, k, v, out)
+        a2_warm = warm_ms(p2, q, k, v, out)
+        sel = p2.info["plan_id"]
+        info = p2.info
+        p2.destroy()
+        row = dict(block=list(block), H=H, N=N, family=c["family"], density=info["density"],
+                   run_coverage=info["run_coverage"], row_skew=info["row_skew"],
+                   plans=len(eligible), base=cat[base]["name"], selected=cat[sel]["name"],
+                   fastest=cat[fastest]["name"], k_a0=lat[base], k_a2=lat[sel], k_best=lat[fastest],
+                   a0_cold_ms=a0_cold, a1_cold_ms=a1_cold, a2_cold_ms=a2_cold,
+                   a0_warm_ms=a0_warm, a2_warm_ms=a2_warm)
+        rows.append(row)
+        log(f"case {ci + 1}/{len(cases)} B={block} H={H} N={N} {c['family']} dens={row['density']:.3f} "
+            f"sel={row['selected']} fastest={row['fastest']} regret={row['k_a2'] / row['k_best']:.3f} "
+            f"A2/A0 kernel x{row['k_a0'] / row['k_a2']:.2f}")
+        del q, k, v, out, Md
+        torch.cuda.empty_cache()
+    return rows
+
+
+def summarize(rows):
+    regret = [r["k_a2"] / r["k_best"] for r in rows]
+    sp_a2 = [r["k_a0"] / r["k_a2"] for r in rows]
+    sp_a1 = [r["k_a0"] / r["k_best"] for r in rows]
+    wins = sum(1 for s in sp_a2 if s > 1 + TIE)
+    losses = sum(1 for s in sp_a2 if s < 1 - TIE)
+    regret_sorted = sorted(regret)
+    p95 = regret_sorted[min(len(regret) - 1, int(math.ceil(0.95 * len(regret))) - 1)]
+    return {
+        "cases": len(rows),
+        "kernel_speedup_over_direct_gm": {"A2_table": _gm(sp_a2), "A1_exhaustive": _gm(sp_a1)},
+        "selection_regret": {"gm": _gm(regret), "p95": p95, "max": max(regret),
+                             "within_3pct_share": sum(1 for x in regret if x <= 1 + TIE) / len(rows)},
+        "A2_vs_A0_kernel_wins_ties_losses": [wins, len(rows) - wins - losses, losses],
+        "cold_request_speedup_gm": {"A2_over_A0": _gm([r["a0_cold_ms"] / r["a2_cold_ms"] for r in rows]),
+                                    "A2_over_A1": _gm([r["a1_cold_ms"] / r["a2_cold_ms"] for r in rows]),
+                                    "A1_over_A0": _gm([r["a0_cold_ms"] / r["a1_cold_ms"] for r in rows])},
+        "warm_repeat_speedup_gm": {"A2_over_A0": _gm([r["a0_warm_ms"] / r["a2_warm_ms"] for r in rows])},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=None, help="write {summary, rows} as JSON here")
+    ap.add_argument("--quick", action="store_true")
+    a = ap.parse_args()
+    cases, make_mask = heldout(a.quick)
+    rows = run(cases, make_mask, log=lambda s: print(s, flush=True))
+    summ = summarize(rows)
+    print(json.dumps(summ, indent=1), flush=True)
+    if a.out:
+        with open(a.out, "w") as f:
+            json.dump({"summary": summ, "rows": rows}, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()

@@ -93,3 +93,21 @@ def test_corpus_masks_have_requested_shape(fam):
     M = pt.make_mask(c)
     assert M.shape == (4, 64, 64) and M.dtype.name == "uint8"
     assert 0.02 < (M != 0).mean() < 0.6
+
+
+def test_ablation_summary_metrics():
+    from dynamic_block_sparse_bsa_amd import ablation
+    rows = [dict(k_a0=2.0, k_a2=1.0, k_best=1.0, a0_cold_ms=3.0, a1_cold_ms=30.0, a2_cold_ms=2.0,
+                 a0_warm_ms=2.5, a2_warm_ms=1.5),
+            dict(k_a0=1.0, k_a2=1.1, k_best=1.0, a0_cold_ms=2.0, a1_cold_ms=20.0, a2_cold_ms=2.2,
+                 a0_warm_ms=1.2, a2_warm_ms=1.3),
+            dict(k_a0=1.0, k_a2=1.01, k_best=1.0, a0_cold_ms=2.0, a1_cold_ms=10.0, a2_cold_ms=2.0,
+                 a0_warm_ms=1.0, a2_warm_ms=1.0)]
+    s = ablation.summarize(rows)
+    assert s["cases"] == 3
+    assert s["selection_regret"]["max"] == pytest.approx(1.1)
+    assert s["selection_regret"]["within_3pct_share"] == pytest.approx(2 / 3)
+    # A2 vs A0 kernel speedups 2.0 (win), 1/1.1 (loss), 1/1.01 (tie, inside the 3% band)
+    assert s["A2_vs_A0_kernel_wins_ties_losses"] == [1, 1, 1]
+    assert s["kernel_speedup_over_direct_gm"]["A2_table"] == pytest.approx((2.0 / 1.1 / 1.01) ** (1 / 3))
+    assert s["cold_request_speedup_gm"]["A2_over_A1"] == pytest.approx((15 * (20 / 2.2) * 5) ** (1 / 3))
