@@ -48,7 +48,8 @@ class PlanInfo(ctypes.Structure):
 
 
 class CatalogEntry(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("id", "tile_q", "tile_kv", "d", "split", "xcd_remap")] + \
+    _fields_ = [(n, ctypes.c_int32) for n in ("id", "tile_q", "tile_kv", "d", "split", "xcd_remap",
+                                              "order")] + \
         [("name", ctypes.c_char * 48)]
 
 
@@ -74,6 +75,7 @@ def _load():
     L.bsa_plan_get_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
     L.bsa_plan_export_tiles.argtypes = [P, P, P, P, P, i64, ctypes.POINTER(i64)]
     L.bsa_plan_export_csr.argtypes = [P, P, P, i64]
+    L.bsa_plan_export_tasks.argtypes = [P, P, P, P, P, P, i64, ctypes.POINTER(i64)]
     L.bsa_catalog_size.restype = i32
     L.bsa_catalog_get.argtypes = [i32, ctypes.POINTER(CatalogEntry)]
     L.bsa_plan_eligible.argtypes = [i32, ctypes.POINTER(Request), ctypes.POINTER(i32)]
@@ -86,6 +88,7 @@ def _load():
     L.bsa_status_string.argtypes = [i32]
     for f in ("bsa_plan_create", "bsa_run", "bsa_run_timed", "bsa_plan_destroy",
               "bsa_plan_get_info", "bsa_plan_export_tiles", "bsa_plan_export_csr",
+              "bsa_plan_export_tasks",
               "bsa_catalog_get", "bsa_plan_eligible", "bsa_select", "bsa_table_load",
               "bsa_base_plan"):
         getattr(L, f).restype = i32
@@ -144,6 +147,20 @@ class Plan:
                 np.empty(n, np.uint32)]
         ptrs = [a.ctypes.data_as(ctypes.c_void_p) for a in arrs]
         _check(L.bsa_plan_export_tiles(self.handle, *ptrs, n, ctypes.byref(cnt)))
+        return tuple(arrs)
+
+    def export_tasks(self):
+        """numpy arrays (head, q_tile, begin, end, slot) of the tasks in dispatch order."""
+        import numpy as np
+        L = _load()
+        cnt = ctypes.c_int64(0)
+        st = L.bsa_plan_export_tasks(self.handle, None, None, None, None, None, 0, ctypes.byref(cnt))
+        n = cnt.value
+        if st != 0 and n == 0:
+            _check(st)
+        arrs = [np.empty(n, np.int32) for _ in range(5)]
+        ptrs = [a.ctypes.data_as(ctypes.c_void_p) for a in arrs]
+        _check(L.bsa_plan_export_tasks(self.handle, *ptrs, n, ctypes.byref(cnt)))
         return tuple(arrs)
 
     def export_csr(self):
@@ -220,7 +237,7 @@ def catalog():
         e = CatalogEntry()
         _check(L.bsa_catalog_get(i, ctypes.byref(e)))
         res.append(dict(id=e.id, tile_q=e.tile_q, tile_kv=e.tile_kv, d=e.d, split=e.split,
-                        xcd_remap=e.xcd_remap, name=e.name.decode()))
+                        xcd_remap=e.xcd_remap, order=e.order, name=e.name.decode()))
     return res
 
 

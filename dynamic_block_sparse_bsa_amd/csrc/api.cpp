@@ -155,9 +155,10 @@ int wg_per_cu_cached(int tq, int tkv, int d) {
   return n;
 }
 
-// Split-K rule of the "balance" organization: a query tile's traversal is cut
-// when it holds more entries than the even share of all entries over the
-// resident workgroup slots of the device (at least 4 entries per partition).
+// Split-K rule of the "balance" organizations: a query tile's traversal is cut
+// when it holds more entries than 1/split of the even share of all entries
+// over the resident workgroup slots of the device (at least 4 entries per
+// partition).
 struct PlanShape {
   DimMap mq, mk;
   int split = 0;           // entries per partition, 0 = never split
@@ -182,7 +183,7 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
     split = r.force_split;
   } else if (r.force_split < 0 && e.split) {
     const int64_t slots = (int64_t)device_cus(dev) * wg_per_cu_cached(e.tq, e.tkv, e.d);
-    split = (int)std::max<int64_t>(4, cdiv(std::max<int64_t>(W, 1), slots));
+    split = (int)std::max<int64_t>(4, cdiv(std::max<int64_t>(W, 1), slots * e.split));
     if (row_max <= split) split = 0;
   }
   p.split = split;
@@ -283,6 +284,7 @@ bsa_status bsa_catalog_get(int32_t id, bsa_catalog_entry* out) {
   out->d = e.d;
   out->split = e.split;
   out->xcd_remap = e.xcd_remap;
+  out->order = e.order;
   std::snprintf(out->name, sizeof out->name, "%s", e.name.c_str());
   return BSA_OK;
 }
@@ -462,8 +464,12 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->parts));
   HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->slot_off));
   HIP_TRY(pool_alloc(p->dev, sizeof(Task) * (size_t)std::max<int64_t>(shape.tasks_upper, 1), &p->tasks));
+  const int64_t max_len = shape.split > 0 ? shape.split
+                                          : std::min<int64_t>((int64_t)shape.mq.coarsen * p->stats.max_row_nnz,
+                                                              1 << 30);
   HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split,
-                       (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr, dst, s));
+                       chosen->order, (int32_t)max_len, (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr,
+                       dst, s));
   if (shape.slots_upper > 0) HIP_TRY(pool_alloc(p->dev, (size_t)shape.ws_bytes, &p->ws));
   const int64_t gran = chosen->xcd_remap > 0 ? 8 * (int64_t)chosen->xcd_remap : 1;
   p->grid = cdiv(std::max<int64_t>(shape.tasks_upper, 1), gran) * gran;
@@ -652,6 +658,29 @@ bsa_status bsa_plan_export_tiles(const bsa_plan* p, int32_t* head, int32_t* q_ti
   const_cast<bsa_plan*>(p)->info.n_items = nitems;
   const_cast<bsa_plan*>(p)->info.n_tasks = (int64_t)nt;
   if (n > cap) return fail(BSA_ERR_INVALID_ARG, "capacity %lld < %lld tiles", (long long)cap, (long long)n);
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_export_tasks(const bsa_plan* p, int32_t* head, int32_t* q_tile, int32_t* begin,
+                                 int32_t* end, int32_t* slot, int64_t cap, int64_t* count) {
+  if (!p || !count) return fail(BSA_ERR_INVALID_ARG, "NULL argument");
+  HIP_TRY(hipDeviceSynchronize());
+  MaskStats st{};
+  HIP_TRY(hipMemcpy(&st, p->stats_dev.ptr, sizeof st, hipMemcpyDeviceToHost));
+  const int64_t nt = (int64_t)st.n_tasks;
+  *count = nt;
+  if (nt > cap) return fail(BSA_ERR_INVALID_ARG, "capacity %lld < %lld tasks", (long long)cap, (long long)nt);
+  if (nt == 0) return BSA_OK;
+  if (!head || !q_tile || !begin || !end || !slot) return fail(BSA_ERR_INVALID_ARG, "NULL array");
+  std::vector<Task> tasks((size_t)nt);
+  HIP_TRY(hipMemcpy(tasks.data(), p->tasks.ptr, sizeof(Task) * (size_t)nt, hipMemcpyDeviceToHost));
+  for (int64_t i = 0; i < nt; ++i) {
+    head[i] = tasks[i].head;
+    q_tile[i] = tasks[i].qtile;
+    begin[i] = tasks[i].begin;
+    end[i] = tasks[i].end;
+    slot[i] = tasks[i].slot;
+  }
   return BSA_OK;
 }
 

@@ -76,22 +76,33 @@ __global__ __launch_bounds__(256) void k_row_count(const uint8_t* __restrict__ m
   }
 }
 
-// Block-wide exclusive scan of one int32 per thread (1024 threads); returns
-// the exclusive prefix and sets *tot to the block total.
+// Inclusive scan of one int32 per lane across the wave (64 lanes).
+__device__ inline int32_t wave_scan(int32_t x) {
+  const int l = (int)lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (l >= off) x += y;
+  }
+  return x;
+}
+
+// Block-wide exclusive scan of one int32 per thread (1024 threads = 16
+// waves); returns the exclusive prefix and sets *tot to the block total.
+// Uses lds[0..31]; consecutive calls need no barrier in between.
 __device__ int32_t block_scan(int32_t v, int32_t* lds, int32_t* tot) {
   const int t = threadIdx.x;
-  lds[t] = v;
+  const int l = t & 63, w = t >> 6;
+  const int32_t x = wave_scan(v);
+  if (l == 63) lds[w] = x;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
-    const int32_t x = t >= off ? lds[t - off] : 0;
-    __syncthreads();
-    lds[t] += x;
-    __syncthreads();
+  if (w == 0) {
+    const int32_t s = wave_scan(l < 16 ? lds[l] : 0);
+    if (l < 16) lds[16 + l] = s;
   }
-  const int32_t incl = lds[t];
-  *tot = lds[1023];
   __syncthreads();
-  return incl - v;
+  *tot = lds[31];
+  return (w > 0 ? lds[15 + w] : 0) + x - v;
 }
 
 // Exclusive scan of n int32 values by one workgroup of 1024 threads; out has
@@ -103,7 +114,7 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
                                                int32_t* __restrict__ out, int32_t n,
                                                const RowPartial* __restrict__ part, int32_t npart,
                                                MaskStats* st, MaskStats* host_st) {
-  __shared__ int32_t lds[1024];
+  __shared__ int32_t lds[32];
   const int t = threadIdx.x;
   int32_t carry = 0;
   for (int base = 0; base < n; base += 4096) {
@@ -122,9 +133,10 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
   }
   if (t == 0) out[n] = carry;
   if (st) {
-    // reduce the partial statistics: thread t folds partials t, t+1024, ...
-    __shared__ unsigned long long s_long[1024];
-    __shared__ unsigned s_max[1024], s_empty[1024];
+    // reduce the partial statistics: thread t folds partials t, t+1024, ...,
+    // then a butterfly per wave and one thread over the 16 wave results
+    __shared__ unsigned long long s_long[16];
+    __shared__ unsigned s_max[16], s_empty[16];
     unsigned long long lg = 0;
     unsigned mx = 0, em = 0;
     for (int i = t; i < npart; i += 1024) {
@@ -132,17 +144,24 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
       mx = max(mx, part[i].max_row);
       em += part[i].empty;
     }
-    s_long[t] = lg;
-    s_max[t] = mx;
-    s_empty[t] = em;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lg += __shfl_xor(lg, off, 64);
+      mx = max(mx, (unsigned)__shfl_xor((int)mx, off, 64));
+      em += (unsigned)__shfl_xor((int)em, off, 64);
+    }
+    if ((t & 63) == 0) {
+      s_long[t >> 6] = lg;
+      s_max[t >> 6] = mx;
+      s_empty[t >> 6] = em;
+    }
     __syncthreads();
-    for (int off = 512; off > 0; off >>= 1) {
-      if (t < off) {
-        s_long[t] += s_long[t + off];
-        s_max[t] = max(s_max[t], s_max[t + off]);
-        s_empty[t] += s_empty[t + off];
+    if (t == 0) {
+      for (int w = 1; w < 16; ++w) {
+        s_long[0] += s_long[w];
+        s_max[0] = max(s_max[0], s_max[w]);
+        s_empty[0] += s_empty[w];
       }
-      __syncthreads();
     }
     if (t == 0) {
       MaskStats r;
@@ -248,35 +267,84 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
 // ceil(n / split) contiguous partitions of near-equal size (split == 0 never
 // splits); every query tile gets at least one task, so rows without entries
 // still write zeros.  Writes, per query tile, its partition count and first
-// workspace slot (for the merge kernel), the tasks in query-tile order, and
-// the task count into st->n_tasks.
+// workspace slot (for the merge kernel), the tasks, and the task count into
+// st->n_tasks.
+//
+// Traversal order (paper section 3, task organization): order == 0 lists the
+// tasks in query-tile order; order == 1 lists them longest first, so that the
+// in-order dispatch of workgroups approximates a longest-processing-time
+// schedule and the short tasks fill the tail.  Lengths (entries) are counted
+// into kLenBuckets buckets -- exact lengths while max_len < kLenBuckets, else
+// proportional buckets of max_len -- and placed by a counting sort.  Within a
+// bucket, tasks of an earlier 4096-tile chunk of the walk come first; inside
+// a chunk their order follows the LDS atomics.  Every task writes a fixed
+// part of the output (split partials a fixed workspace slot), so the order
+// changes timing, not results.
+constexpr int kLenBuckets = 1024;
+
+struct RowTasks {
+  int h, qt, b, e, p, chunk;
+};
+
+__device__ inline RowTasks row_tasks(const int32_t* __restrict__ trow_ptr, int g, int nqt_head,
+                                     int ntr, int refine_q, int split) {
+  RowTasks r;
+  r.h = g / nqt_head;
+  r.qt = g - r.h * nqt_head;
+  const int tr = r.qt / refine_q;
+  r.b = trow_ptr[r.h * ntr + tr];
+  r.e = trow_ptr[r.h * ntr + tr + 1];
+  const int n = r.e - r.b;
+  r.p = (split > 0 && n > split) ? (n + split - 1) / split : 1;
+  r.chunk = (n + r.p - 1) / r.p;
+  return r;
+}
+
+__device__ inline int len_bucket(int len, int max_len) {
+  // descending length -> ascending bucket index
+  len = min(len, max_len);
+  const int k = max_len < kLenBuckets ? len : (int)(((long long)len * (kLenBuckets - 1)) / max_len);
+  return kLenBuckets - 1 - k;
+}
+
+__device__ inline Task make_task(const RowTasks& r, int i, int slot0) {
+  Task tk;
+  tk.head = r.h;
+  tk.qtile = r.qt;
+  tk.begin = min(r.e, r.b + i * r.chunk);
+  tk.end = min(r.e, r.b + (i + 1) * r.chunk);
+  tk.slot = r.p > 1 ? slot0 + i : -1;
+  tk.pad0 = tk.pad1 = tk.pad2 = 0;
+  return tk;
+}
+
 __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow_ptr, int32_t H,
                                                 int32_t nqt_head, int32_t ntr, int32_t refine_q,
-                                                int32_t split, int32_t* __restrict__ parts,
+                                                int32_t split, int32_t order, int32_t max_len,
+                                                int32_t* __restrict__ parts,
                                                 int32_t* __restrict__ slot_base,
                                                 Task* __restrict__ tasks, MaskStats* st) {
-  __shared__ int32_t lds[1024];
+  __shared__ int32_t lds[32];
+  __shared__ int32_t cursor[kLenBuckets];
   const int t = threadIdx.x;
   const int nqt = H * nqt_head;
+  max_len = max(max_len, 1);
+  if (order) cursor[t] = 0;
+  __syncthreads();
+  // pass 1: partition counts and workspace slots in query-tile order; the
+  // tasks themselves (query-tile order) or their length histogram
   int32_t carry_t = 0, carry_s = 0;
   for (int base = 0; base < nqt; base += 4096) {
     const int g0 = base + 4 * t;
-    int32_t p[4], b[4], e[4];
+    RowTasks r[4];
     int32_t sum_t = 0, sum_s = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int g = g0 + k;
-      p[k] = 0;
-      b[k] = e[k] = 0;
-      if (g < nqt) {
-        const int h = g / nqt_head;
-        const int tr = (g - h * nqt_head) / refine_q;
-        b[k] = trow_ptr[h * ntr + tr];
-        e[k] = trow_ptr[h * ntr + tr + 1];
-        const int n = e[k] - b[k];
-        p[k] = (split > 0 && n > split) ? (n + split - 1) / split : 1;
-        sum_t += p[k];
-        sum_s += p[k] > 1 ? p[k] : 0;
+      r[k].p = 0;
+      if (g0 + k < nqt) {
+        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split);
+        sum_t += r[k].p;
+        sum_s += r[k].p > 1 ? r[k].p : 0;
       }
     }
     int32_t tot_t, tot_s;
@@ -286,29 +354,57 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
     for (int k = 0; k < 4; ++k) {
       const int g = g0 + k;
       if (g >= nqt) break;
-      const int h = g / nqt_head;
-      const int qt = g - h * nqt_head;
-      const int n = e[k] - b[k];
-      const int chunk = (n + p[k] - 1) / p[k];
-      parts[g] = p[k];
+      parts[g] = r[k].p;
       slot_base[g] = off_s;
-      for (int i = 0; i < p[k]; ++i) {
-        Task tk;
-        tk.head = h;
-        tk.qtile = qt;
-        tk.begin = min(e[k], b[k] + i * chunk);
-        tk.end = min(e[k], b[k] + (i + 1) * chunk);
-        tk.slot = p[k] > 1 ? off_s + i : -1;
-        tk.pad0 = tk.pad1 = tk.pad2 = 0;
-        tasks[off_t + i] = tk;
+      if (order) {
+        for (int i = 0; i < r[k].p; ++i) {
+          const Task tk = make_task(r[k], i, off_s);
+          atomicAdd(&cursor[len_bucket(tk.end - tk.begin, max_len)], 1);
+        }
+      } else {
+        for (int i = 0; i < r[k].p; ++i) tasks[off_t + i] = make_task(r[k], i, off_s);
       }
-      off_t += p[k];
-      off_s += p[k] > 1 ? p[k] : 0;
+      off_t += r[k].p;
+      off_s += r[k].p > 1 ? r[k].p : 0;
     }
     carry_t += tot_t;
     carry_s += tot_s;
   }
   if (t == 0) st->n_tasks = (unsigned long long)carry_t;
+  if (!order) return;
+  // bucket starts, then pass 2 places every task at its bucket's cursor
+  __syncthreads();
+  int32_t tot;
+  const int32_t start = block_scan(cursor[t], lds, &tot);
+  cursor[t] = start;
+  __syncthreads();
+  carry_s = 0;
+  for (int base = 0; base < nqt; base += 4096) {
+    const int g0 = base + 4 * t;
+    RowTasks r[4];
+    int32_t sum_s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r[k].p = 0;
+      if (g0 + k < nqt) {
+        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split);
+        sum_s += r[k].p > 1 ? r[k].p : 0;
+      }
+    }
+    int32_t tot_s;
+    int32_t off_s = carry_s + block_scan(sum_s, lds, &tot_s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (g0 + k >= nqt) break;
+      for (int i = 0; i < r[k].p; ++i) {
+        const Task tk = make_task(r[k], i, off_s);
+        tasks[atomicAdd(&cursor[len_bucket(tk.end - tk.begin, max_len)], 1)] = tk;
+      }
+      off_s += r[k].p > 1 ? r[k].p : 0;
+    }
+    carry_s += tot_s;
+    __syncthreads();  // this chunk's tasks precede the next chunk's in each bucket
+  }
 }
 
 }  // namespace
@@ -347,10 +443,11 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
 }
 
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
-                        int32_t refine_q, int32_t split, int32_t* parts, int32_t* slot_base,
-                        Task* tasks, MaskStats* st, hipStream_t s) {
+                        int32_t refine_q, int32_t split, int32_t order, int32_t max_len,
+                        int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
+                        hipStream_t s) {
   hipLaunchKernelGGL(k_tasks, dim3(1), dim3(1024), 0, s, trow_ptr, H, nqt_head, ntr, refine_q, split,
-                     parts, slot_base, tasks, st);
+                     order, max_len, parts, slot_base, tasks, st);
   return hipGetLastError();
 }
 

@@ -104,8 +104,10 @@ typedef struct {
 typedef struct {
   int32_t id;
   int32_t tile_q, tile_kv, d;
-  int32_t split;        /* 0 = never split, 1 = balance rule                    */
+  int32_t split;        /* 0 = never split; s >= 1 = balance rule, partitions of
+                           at most 1/s of the even share of entries per slot   */
   int32_t xcd_remap;    /* > 0: runs of this many consecutive tasks per XCD      */
+  int32_t order;        /* 0 = query-tile order, 1 = longest task first          */
   char name[48];
 } bsa_catalog_entry;
 
@@ -148,6 +150,18 @@ bsa_status bsa_plan_get_info(const bsa_plan* plan, bsa_plan_info* info);
  * cap is too small (count still set).  For coverage checks only. */
 bsa_status bsa_plan_export_tiles(const bsa_plan* plan, int32_t* head, int32_t* q_tile,
                                  int32_t* kv_tile, uint32_t* bits, int64_t cap, int64_t* count);
+
+/* Export the plan's task list in dispatch order (paper section 3: the task
+ * organization's grouping, traversal order and K/V partitions) to host arrays
+ * of capacity `cap`: head, query-tile index, first and one-past-last entry of
+ * the tile-list row (offsets into the plan's tile list, whose row for query
+ * tile qt of head h is h * rows_per_head + qt / refine_q) and the split-K
+ * workspace slot (-1 when the query tile is not split).  *count receives the
+ * number of tasks; BSA_ERR_INVALID_ARG if cap is too small (count still set).
+ * Synchronizes the device.  For organization checks only. */
+bsa_status bsa_plan_export_tasks(const bsa_plan* plan, int32_t* head, int32_t* q_tile,
+                                 int32_t* begin, int32_t* end, int32_t* slot, int64_t cap,
+                                 int64_t* count);
 
 /* Copy the shared block-CSR (row offsets [H*ceil(N/B_Q)+1] and column
  * indices [nnz_blocks]) to host arrays. */

@@ -1,0 +1,107 @@
+"""GPU: task organizations (grouping, traversal order, K/V partitions).
+
+Tessera paper, section 3 (task organization: grouping, traversal order,
+number of K/V reduction partitions) and section 4.3 ("Grouping and
+traversal", "Split-K").  For every catalog plan whose tiles neither coarsen
+nor merge logical blocks on the query side (so a query tile's tile-list row
+is its logical row of the shared block-CSR), the exported task list is
+checked against the organization's definition:
+
+* every query tile's row of n entries is cut into p = ceil(n / split)
+  contiguous partitions of ceil(n / p) entries (one task when split == 0 or
+  n <= split; rows without entries still get one empty task);
+* split partitions own distinct, consecutive workspace slots, unsplit tasks
+  none;
+* query-tile order lists tasks by (head, query tile, begin); longest-first
+  order lists the same tasks by non-increasing length.
+
+The masks are large enough (more than 4096 query tiles) that the task
+builder walks several chunks; sampled output rows of each longest-first plan
+are checked against the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_bsa_amd as bsa
+from oracle import attention as oatt
+from workloads import gen
+
+from bsa_testutil import MAX_ERR, MEAN_ERR
+
+pytestmark = pytest.mark.gpu
+
+
+def _expected_tasks(rp, H, nqb, nqt_head, refine_q, split):
+    out = []
+    for h in range(H):
+        for qt in range(nqt_head):
+            i = h * nqb + qt // refine_q
+            b, e = int(rp[i]), int(rp[i + 1])
+            n = e - b
+            p = -(-n // split) if (split > 0 and n > split) else 1
+            ch = -(-n // p)
+            for j in range(p):
+                out.append((h, qt, min(e, b + j * ch), min(e, b + (j + 1) * ch), p > 1))
+    return out
+
+
+CASES = [((64, 64), 40000, 8), ((128, 128), 9000, 6)]
+
+
+@pytest.mark.parametrize("block,N,H", CASES)
+def test_task_organizations(block, N, H):
+    d = 128
+    M = gen.mask_clustered(H, N, *block, seed=4242 + N, rho=(0.05, 0.45), p_empty_head=0.25)
+    nqb = M.shape[1]
+    dev = torch.device("cuda")
+    Md = torch.from_numpy(np.ascontiguousarray(M)).to(dev)
+    q = k = v = None
+    checked = 0
+    for e in bsa.catalog():
+        if not bsa.eligible(e["id"], H, N, d, block):
+            continue
+        p = bsa.plan(Md, block, H, N, d, force_plan=e["id"])
+        info = p.info
+        if info["coarsen_q"] != 1 or info["coarsen_kv"] != 1:
+            p.destroy()
+            continue
+        rp, _ = p.export_csr()
+        head, qt, beg, end, slot = p.export_tasks()
+        nqt_head = -(-N // info["tile_q"])
+        exp = _expected_tasks(rp, H, nqb, nqt_head, info["refine_q"], info["split_items"])
+        got = list(zip(head.tolist(), qt.tolist(), beg.tolist(), end.tolist(), (slot >= 0).tolist()))
+        label = f"{e['name']} B={block} N={N}"
+        assert sorted(got) == sorted(exp), f"{label}: task multiset"
+        if e["order"] == 0 and e["xcd_remap"] == 0:
+            assert got == exp, f"{label}: query-tile order"
+        if e["order"] == 1:
+            ln = end - beg
+            assert (np.diff(ln) <= 0).all(), f"{label}: not longest first"
+        # split slots: distinct, consecutive per query tile in partition order
+        s = slot[slot >= 0]
+        assert len(np.unique(s)) == len(s), f"{label}: shared slot"
+        o = np.lexsort((beg, qt, head))
+        same = (head[o][1:] == head[o][:-1]) & (qt[o][1:] == qt[o][:-1])
+        assert (np.diff(slot[o])[same] == 1).all(), f"{label}: slots not consecutive per query tile"
+        assert (slot[o][1:][same] >= 0).all(), f"{label}: split tile with an unslotted part"
+        if e["order"] == 1:
+            if q is None:
+                q, k, v = gen.qkv(H, N, d, (11, 12, 13))
+                qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+                rng = np.random.default_rng(N)
+                rows = {h: np.unique(np.concatenate([rng.integers(0, N, 96), [N - 1]]))
+                        for h in range(H)}
+                ref = oatt.attention_rows(q, k, v, M, block[0], block[1], rows)
+            out = torch.full((H, N, d), float("nan"), dtype=torch.bfloat16, device=dev)
+            bsa.run(p, qd, kd, vd, out)
+            torch.cuda.synchronize()
+            assert not torch.isnan(out).any().item(), f"{label}: unwritten rows"
+            err = np.concatenate([np.abs(out[h, torch.from_numpy(r).to(dev)].float().cpu().numpy()
+                                         .astype(np.float64) - ref[h]) for h, r in rows.items()])
+            assert err.max() <= MAX_ERR and err.mean() <= MEAN_ERR, \
+                f"{label}: max {err.max():.3e} mean {err.mean():.3e}"
+        p.destroy()
+        checked += 1
+    assert checked >= 6

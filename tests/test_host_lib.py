@@ -26,7 +26,10 @@ def test_library_exports_header_symbols():
 
 def test_catalog_and_hash():
     cat = bsa.catalog()
-    assert 14 <= len(cat) <= 40
+    shapes = {(e["tile_q"], e["tile_kv"], e["d"]) for e in cat}
+    orgs = {(e["split"], e["xcd_remap"], e["order"]) for e in cat}
+    assert len(cat) == len(shapes) * len(orgs)  # every organization of every kernel shape
+    assert {(1, 0, 0), (0, 0, 0), (1, 0, 1), (2, 0, 1), (0, 0, 1)} <= orgs
     names = [e["name"] for e in cat]
     assert len(set(names)) == len(names)
     assert re.fullmatch(r"[0-9a-f]{16}", bsa.catalog_hash())
@@ -36,7 +39,7 @@ def test_base_plan_direct_or_smallest_refined():
     cat = {e["id"]: e for e in bsa.catalog()}
     e = cat[bsa.base_plan(8, 8192, 128, (128, 128))]
     assert (e["tile_q"], e["tile_kv"]) == (128, 128)  # Direct when the catalog has T = B
-    assert e["split"] == 1 and e["xcd_remap"] == 0  # default organization
+    assert e["split"] == 1 and e["xcd_remap"] == 0 and e["order"] == 0  # default organization
     e = cat[bsa.base_plan(24, 115200, 128, (32, 128))]
     assert e["tile_q"] * e["tile_kv"] == min(
         c["tile_q"] * c["tile_kv"] for c in cat.values()
@@ -68,7 +71,8 @@ def test_builtin_table_is_versioned_and_covers_workload_keys():
 
 def test_eligibility_rules():
     cat = bsa.catalog()
-    by = {(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"]): e["id"] for e in cat}
+    by = {(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"]): e["id"] for e in cat
+          if e["order"] == 0}
     # coarsening B_Q = 16 into a 64-row tile would split a wave across logical rows
     assert not bsa.eligible(by[(64, 64, 128, 1, 0)], 1, 1024, 128, (16, 64))
     assert bsa.eligible(by[(64, 64, 128, 1, 0)], 1, 1024, 128, (32, 64))
