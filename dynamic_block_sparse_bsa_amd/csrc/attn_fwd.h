@@ -126,6 +126,19 @@ __device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
   return r;
 }
 
+// ds_read_b128 from inline assembly, for the same reason: the K fragment
+// reads then run several MFMAs ahead of their use with counted waits.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+  u32x4 r;
+  if constexpr (OFF < 65536) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  } else {
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr + (uint32_t)OFF));
+  }
+  return r;
+}
+
 // s_waitcnt lgkmcnt(CNT) that also ties the given registers, so no use of
 // them can be scheduled above the wait.  LDS operations complete in issue
 // order, so CNT = number of LDS reads issued after the ones being waited for.
@@ -144,6 +157,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(CNT >= 0 && CNT < 64, "vmcnt field is 6 bits");
   __builtin_amdgcn_s_waitcnt((CNT & 15) | ((CNT >> 4) << 14) | 0x0F70);
 }
+
+// Entry-point choice (see the entry points below): 32-key tiles at d = 128
+// with at most 128 queries run three waves per SIMD.
+template <int TQ, int TKV, int D>
+constexpr bool use_w3() { return TKV == 32 && D == 128 && TQ == 128; }
+// K fragments read ahead of their MFMA: deeper where registers allow.
+template <int TQ, int TKV, int D>
+constexpr int kpf_depth() { return use_w3<TQ, TKV, D>() ? 2 : 4; }
 
 template <int TQ, int TKV, int D>
 __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
@@ -336,6 +357,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   // LDS byte addresses of the transposed V reads per d-block (the stage and
   // row offsets are added as instruction immediates)
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)smem_arr;
+  uint32_t kaddr[S::DK];
+#pragma unroll
+  for (int c = 0; c < S::DK; ++c) kaddr[c] = lds0 + (uint32_t)(kbase ^ (c << 5));
   uint32_t vaddr0[S::DB], vaddr1[S::DB];
 #pragma unroll
   for (int b = 0; b < S::DB; ++b) {
@@ -372,14 +396,26 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 
     if (wbits != 0u && cur_kv0 < N) {
       // ---- S^T = K Q^T ---------------------------------------------------
+      // K fragment i = (st, c) is read KPF fragments ahead of its MFMA.
       f32x16 s[S::NST];
-#pragma unroll
-      for (int st = 0; st < S::NST; ++st) {
-#pragma unroll
-        for (int c = 0; c < S::DK; ++c) {
-          const bf16x8 kf = *(const lds_bf16x8*)(kl + st * 32 * (D * 2) + (kbase ^ (c << 5)));
+      {
+        constexpr int NK = S::NST * S::DK;
+        constexpr int KPF = NK < kpf_depth<TQ, TKV, D>() ? NK : kpf_depth<TQ, TKV, D>();
+        u32x4 kr[KPF];
+        auto kread = [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          kr[i % KPF] = ds_read_b128<buf * STAGE + (i / S::DK) * 32 * (D * 2)>(kaddr[i % S::DK]);
+        };
+        sfor<KPF>(kread);
+        sfor<NK>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int st = i / S::DK, c = i % S::DK;
+          constexpr int later = (NK - 1 - i) < (KPF - 1) ? (NK - 1 - i) : (KPF - 1);
+          lgkm_wait<later>(kr[i % KPF]);
+          const bf16x8 kf = __builtin_bit_cast(bf16x8, kr[i % KPF]);
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? cm : s[st], 0, 0, 0);
-        }
+          if constexpr (i + KPF < NK) kread(std::integral_constant<int, i + KPF>{});
+        });
       }
       // ---- masking: inactive logical blocks of the tile, keys >= N ---------
       // A 16-key group (st, v/8) never straddles a logical K/V block (B_KV >=
@@ -445,40 +481,47 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
             l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run, false);
           }
       // ---- O^T += V^T P^T; V^T fragments via LDS transpose reads ----------
-      // The reads of d-block b+1 are in flight while the MFMAs of block b run.
+      // The product runs in chunks of (one 32-wide d-block) x (up to two
+      // 32-key sub-tiles); the reads of chunk q+1 are in flight while the
+      // MFMAs of chunk q run (two chunk buffers of at most 16 registers).
       constexpr int VOFF = buf * STAGE + S::KBYTES;  // V tile of this stage
-      constexpr int NVR = S::NST * 2 * 2;           // transposed reads per d-block
-      u32x2 vr[2][S::NST][2][2];
-      auto vread = [&](auto bc, auto slot) {
-        constexpr int b = decltype(bc)::value;
-        sfor<S::NST>([&](auto stc) {
-          constexpr int st = decltype(stc)::value;
+      constexpr int NSTG = S::NST < 2 ? S::NST : 2;  // sub-tiles per chunk
+      constexpr int NG = S::NST / NSTG;              // chunks per d-block
+      constexpr int NQ = S::DB * NG;
+      constexpr int NVR = NSTG * 2 * 2;              // transposed reads per chunk
+      u32x2 vr[2][NSTG][2][2];
+      auto vread = [&](auto qc, auto slot) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int b = q / NG, g = q % NG;
+        sfor<NSTG>([&](auto stc) {
+          constexpr int sl = decltype(stc)::value;
           sfor<2>([&](auto c2c) {
             constexpr int c2 = decltype(c2c)::value;
-            constexpr int off = VOFF + (st * 32 + c2 * 16) * (D * 2);
-            vr[decltype(slot)::value][st][c2][0] = ds_read_tr16<off>(vaddr0[b]);
-            vr[decltype(slot)::value][st][c2][1] = ds_read_tr16<off>(vaddr1[b]);
+            constexpr int off = VOFF + ((g * NSTG + sl) * 32 + c2 * 16) * (D * 2);
+            vr[decltype(slot)::value][sl][c2][0] = ds_read_tr16<off>(vaddr0[b]);
+            vr[decltype(slot)::value][sl][c2][1] = ds_read_tr16<off>(vaddr1[b]);
           });
         });
       };
       vread(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-      sfor<S::DB>([&](auto bc) {
-        constexpr int b = decltype(bc)::value;
-        constexpr int cur = b & 1;
-        if constexpr (b + 1 < S::DB) {
-          vread(std::integral_constant<int, b + 1>{}, std::integral_constant<int, cur ^ 1>{});
-          lgkm_wait<(NVR < 16 ? NVR : 15)>(vr[cur]);  // 15: also waits for one of b+1
+      sfor<NQ>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int b = q / NG, g = q % NG;
+        constexpr int cur = q & 1;
+        if constexpr (q + 1 < NQ) {
+          vread(std::integral_constant<int, q + 1>{}, std::integral_constant<int, cur ^ 1>{});
+          lgkm_wait<(NVR < 16 ? NVR : 15)>(vr[cur]);  // 15: also waits for one of q+1
         } else {
           lgkm_wait<0>(vr[cur]);
         }
-        sfor<S::NST>([&](auto stc) {
-          constexpr int st = decltype(stc)::value;
+        sfor<NSTG>([&](auto stc) {
+          constexpr int sl = decltype(stc)::value;
           sfor<2>([&](auto c2c) {
             constexpr int c2 = decltype(c2c)::value;
-            const u32x4 raw = {vr[cur][st][c2][0][0], vr[cur][st][c2][0][1], vr[cur][st][c2][1][0],
-                               vr[cur][st][c2][1][1]};
+            const u32x4 raw = {vr[cur][sl][c2][0][0], vr[cur][sl][c2][0][1], vr[cur][sl][c2][1][0],
+                               vr[cur][sl][c2][1][1]};
             const bf16x8 vf = __builtin_bit_cast(bf16x8, raw);
-            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st][c2], acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g * NSTG + sl][c2], acc[b], 0, 0, 0);
           });
         });
       });
@@ -492,14 +535,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
     bitsq[NSTAGE - 2] = bitsn;
     ++j;
   };
-  while (true) {
-    if (j >= total) break;
+  for (int round = 0; round < total; round += NSTAGE) {
     step(std::integral_constant<int, 0>{});
-    if (j >= total) break;
-    step(std::integral_constant<int, 1>{});
+    if (round + 1 < total) step(std::integral_constant<int, 1>{});
     if constexpr (NSTAGE == 3) {
-      if (j >= total) break;
-      step(std::integral_constant<int, 2>{});
+      if (round + 2 < total) step(std::integral_constant<int, 2>{});
     }
   }
 
@@ -550,9 +590,6 @@ __global__ __launch_bounds__(TQ * 2) __attribute__((amdgpu_waves_per_eu(3)))
 __attribute__((amdgpu_num_vgpr(168))) void attn_fwd_kernel_w3(const AttnArgs a) {
   attn_fwd_body<TQ, TKV, D>(a);
 }
-template <int TQ, int TKV, int D>
-constexpr bool use_w3() { return TKV == 32 && D == 128 && TQ == 128; }
-
 template <int TQ, int TKV, int D>
 hipError_t launch_attn(const AttnArgs& a, int grid, hipStream_t s) {
   if constexpr (use_w3<TQ, TKV, D>())
