@@ -154,8 +154,8 @@ def main():
     def request(i, want_info=False):
         Md, block, _, _ = reqs[i % len(reqs)]
         p = bsa.plan(Md, block, H, N, d, force_plan=args.force_plan, force_split=args.force_split)
+        # returns once the request's last kernel has completed (HIP event wait)
         _, a_ms, m_ms = bsa.run_timed(p, q, k, v, out)
-        torch.cuda.synchronize()
         info = p.info if want_info else None
         p.destroy()
         return a_ms, m_ms, info

@@ -41,12 +41,14 @@ def heldout(quick=False):
     cases = []
     seed = 950000
     keys = [((64, 64), 128), ((128, 128), 128), ((128, 32), 128), ((32, 128), 128)]
-    sizes = [(8, 8192), (4, 32768), (4, 75600)] if not quick else [(4, 8192)]
+    sizes = [(8, 8192), (4, 32768), (4, 75600), (24, 75600)] if not quick else [(4, 8192)]
     dens = [0.05, 0.12, 0.22, 0.35] if not quick else [0.15]
     fams = ["clustered", "iid_mixed", "window", "iid"]
     for block, d in keys:
         for H, N in sizes:
             for i, rho in enumerate(dens):
+                if H >= 16 and i % 2:  # many-head cases: two densities per key
+                    continue
                 fam = fams[(i + H) % 4]
                 if fam == "window" and block[0] != block[1]:
                     fam = "clustered"

@@ -40,7 +40,9 @@ if ROOT not in sys.path:
 
 # feature schema: bucket k of a feature holds bounds[k-1] <= x < bounds[k]
 BOUNDS = {
-    "H": [],
+    # head count: with many heads the task list spans far more K/V than the
+    # caches hold, and organizations that keep neighbouring tiles together win
+    "H": [16.0],
     "N": [12288.0, 49152.0],
     "density": [0.08, 0.2, 0.35],
     "run_coverage": [0.5],
@@ -63,22 +65,26 @@ def corpus(quick=False):
     keys = [((64, 64), 128), ((128, 128), 128), ((128, 32), 128), ((32, 128), 128), ((64, 64), 64)]
     if quick:
         sizes, dens = [(4, 8192), (2, 65536)], [0.1, 0.3]
+        big, big_dens = [(24, 32768)], [0.1]
     else:
         sizes = [(8, 8192), (8, 16384), (8, 32768), (4, 75600), (4, 115200)]
         dens = [0.03, 0.06, 0.1, 0.14, 0.2, 0.28, 0.4, 0.5]
+        # many heads at long sequences (the second head-count bucket)
+        big, big_dens = [(24, 75600), (32, 115200)], [0.06, 0.14, 0.22]
     families = ["clustered", "window", "iid_mixed", "iid"]
     cases = []
     seed = 900000
     for block, d in keys:
-        for H, N in sizes:
-            if d == 64 and N > 32768:
-                continue
-            for i, rho in enumerate(dens):
-                fam = families[(i + N) % 4]
-                if fam == "window" and block[0] != block[1]:
-                    fam = "clustered"
-                cases.append(dict(block=block, d=d, H=H, N=N, family=fam, rho=rho, seed=seed))
-                seed += 1
+        for grid, rhos in ((sizes, dens), (big, big_dens)):
+            for H, N in grid:
+                if d == 64 and N > 32768:
+                    continue
+                for i, rho in enumerate(rhos):
+                    fam = families[(i + N) % 4]
+                    if fam == "window" and block[0] != block[1]:
+                        fam = "clustered"
+                    cases.append(dict(block=block, d=d, H=H, N=N, family=fam, rho=rho, seed=seed))
+                    seed += 1
     return cases
 
 
@@ -194,8 +200,9 @@ def compile_table(records, version):
     groups = {}
     for r in records:
         key = (r["block"][0], r["block"][1], r["d"])
-        reg = (bucket(BOUNDS["N"], r["N"]), bucket(BOUNDS["density"], r["density"]),
-               bucket(BOUNDS["run_coverage"], r["run_coverage"]), bucket(BOUNDS["row_skew"], r["row_skew"]))
+        reg = (bucket(BOUNDS["H"], r["H"]), bucket(BOUNDS["N"], r["N"]),
+               bucket(BOUNDS["density"], r["density"]), bucket(BOUNDS["run_coverage"], r["run_coverage"]),
+               bucket(BOUNDS["row_skew"], r["row_skew"]))
         groups.setdefault(key, {}).setdefault(reg, []).append(r)
     lines = [f"bsa-plan-table {version}", "arch gfx950", f"catalog {bsa.catalog_hash()}"]
     for f in ("H", "N", "density", "run_coverage", "row_skew"):
@@ -213,8 +220,9 @@ def compile_table(records, version):
             if ranking[-1] != base:
                 ranking.append(base)  # every ranking ends with the key's base plan
             lines.append(f"# {len(rs)} cases; best GM {gm[ranking[0]]:.4f} ms")
-            lines.append("regime %d %d %d * %d %d %d %d : %s" % (key[0], key[1], key[2], reg[0], reg[1], reg[2],
-                                                               reg[3], " ".join(names[p] for p in ranking)))
+            hb = str(reg[0]) if BOUNDS["H"] else "*"
+            lines.append("regime %d %d %d %s %d %d %d %d : %s" % (key[0], key[1], key[2], hb, reg[1], reg[2],
+                                                                reg[3], reg[4], " ".join(names[p] for p in ranking)))
     return "\n".join(lines) + "\n"
 
 

@@ -97,8 +97,10 @@ def test_c2_medium():
         p.destroy()
 
 
+# Small and large masks (the last two span several scan tiles and thousands
+# of rows).
 @pytest.mark.parametrize("block,N", [((64, 64), 1024), ((128, 32), 777), ((32, 128), 5000),
-                                     ((64, 64), 70)])
+                                     ((64, 64), 70), ((64, 64), 40000), ((32, 128), 60000)])
 def test_mask_state_matches_oracle(block, N):
     """Block-CSR (bit-exact) and the scalar statistics of the shared mask
     state against the oracle's definitions (density, run coverage)."""

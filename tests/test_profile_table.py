@@ -45,9 +45,9 @@ def test_geometric_mean_ranking_and_validity(tmp_path):
     assert ranking[0] == names[a] and ranking[1] == names[b]
     assert names[c] not in ranking[:2]
     assert ranking[-1] == names[bsa.base_plan(8, 8192, 128, (128, 128))]
-    # regime fields: key, H wildcard, buckets of N, density, run coverage, row skew
+    # regime fields: key, buckets of H, N, density, run coverage, row skew
     f = lines[0].split(" : ")[0].split()
-    assert f[1:4] == ["128", "128", "128"] and f[4] == "*"
+    assert f[1:4] == ["128", "128", "128"] and f[4] == str(pt.bucket(pt.BOUNDS["H"], 8))
     assert f[5:] == [str(pt.bucket(pt.BOUNDS["N"], 8192)), str(pt.bucket(pt.BOUNDS["density"], 0.3)),
                      str(pt.bucket(pt.BOUNDS["run_coverage"], 0.6)),
                      str(pt.bucket(pt.BOUNDS["row_skew"], 1.2))]
@@ -70,9 +70,10 @@ def test_cases_split_by_key_and_buckets():
     recs = [_rec((128, 128), 8192, 0.3, 0.6, 1.0, {i128[0]: 1.0}),
             _rec((128, 128), 8192, 0.3, 0.6, 3.0, {i128[1]: 1.0}),   # row-skew bucket differs
             _rec((128, 128), 100000, 0.3, 0.6, 1.0, {i128[2]: 1.0}),  # N bucket differs
+            _rec((128, 128), 8192, 0.3, 0.6, 1.0, {i128[3]: 1.0}, H=40),  # head-count bucket differs
             _rec((64, 64), 8192, 0.3, 0.6, 1.0, {i64[0]: 1.0})]       # key differs
     text = pt.compile_table(recs, "v2")
-    assert sum(ln.startswith("regime") for ln in text.splitlines()) == 4
+    assert sum(ln.startswith("regime") for ln in text.splitlines()) == 5
 
 
 def test_corpus_seeds_disjoint_from_workloads():
