@@ -27,6 +27,7 @@ more than the parity tolerance on any case is invalid for that case.
 """
 
 import argparse
+import json
 import math
 import os
 import statistics
@@ -165,9 +166,10 @@ def profile(cases, reps=5, warmup=3, log=print):
             info = p.info
             stats = (info["density"], info["run_coverage"], info["row_skew"])
             ts = []
-            for i in range(warmup + reps):
+            nw, nr = (1, 3) if H >= 16 else (warmup, reps)  # many-head cases run 10-100 ms
+            for i in range(nw + nr):
                 _, a_ms, m_ms = bsa.run_timed(p, q, k, v, out)
-                if i >= warmup:
+                if i >= nw:
                     ts.append(a_ms + m_ms)
             torch.cuda.synchronize()
             ok = True
@@ -208,21 +210,33 @@ def compile_table(records, version):
     for f in ("H", "N", "density", "run_coverage", "row_skew"):
         if BOUNDS[f]:
             lines.append(f"bounds {f} " + " ".join(repr(float(x)) for x in BOUNDS[f]))
+    def emit(key, fields, rs):
+        common = set.intersection(*[set(r["latency"]) for r in rs]) if rs else set()
+        if not common:
+            return
+        gm = {pid: math.exp(sum(math.log(r["latency"][pid]) for r in rs) / len(rs)) for pid in common}
+        ranking = sorted(common, key=lambda pid: (gm[pid], pid))[:TOP]
+        base = bsa.base_plan(rs[0]["H"], rs[0]["N"], key[2], (key[0], key[1]))
+        if ranking[-1] != base:
+            ranking.append(base)  # every ranking ends with the key's base plan
+        lines.append(f"# {len(rs)} cases; best GM {gm[ranking[0]]:.4f} ms")
+        lines.append("regime %d %d %d %s : %s" % (key[0], key[1], key[2], " ".join(fields),
+                                                  " ".join(names[p] for p in ranking)))
+
     for key in sorted(groups):
+        # regimes: request-dimension and mask-statistic buckets
         for reg in sorted(groups[key]):
-            rs = groups[key][reg]
-            common = set.intersection(*[set(r["latency"]) for r in rs]) if rs else set()
-            if not common:
-                continue
-            gm = {pid: math.exp(sum(math.log(r["latency"][pid]) for r in rs) / len(rs)) for pid in common}
-            ranking = sorted(common, key=lambda pid: (gm[pid], pid))[:TOP]
-            base = bsa.base_plan(rs[0]["H"], rs[0]["N"], key[2], (key[0], key[1]))
-            if ranking[-1] != base:
-                ranking.append(base)  # every ranking ends with the key's base plan
-            lines.append(f"# {len(rs)} cases; best GM {gm[ranking[0]]:.4f} ms")
             hb = str(reg[0]) if BOUNDS["H"] else "*"
-            lines.append("regime %d %d %d %s %d %d %d %d : %s" % (key[0], key[1], key[2], hb, reg[1], reg[2],
-                                                                reg[3], reg[4], " ".join(names[p] for p in ranking)))
+            emit(key, [hb] + [str(x) for x in reg[1:]], groups[key][reg])
+        # coarser regimes after them (the lookup takes the first match): the
+        # same request-dimension buckets with any mask statistics, then any
+        # request of the key; a request misses only for a key never profiled
+        coarse = {}
+        for reg, rs in groups[key].items():
+            coarse.setdefault(reg[:2], []).extend(rs)
+        for (h, n) in sorted(coarse):
+            emit(key, [str(h) if BOUNDS["H"] else "*", str(n), "*", "*", "*"], coarse[(h, n)])
+        emit(key, ["*"] * 5, [r for rs in groups[key].values() for r in rs])
     return "\n".join(lines) + "\n"
 
 
@@ -231,9 +245,21 @@ def main():
     ap.add_argument("--out", default=os.path.join(HERE, "tables", "gfx950_v1.txt"))
     ap.add_argument("--quick", action="store_true", help="small corpus (smoke test of the tool)")
     ap.add_argument("--version", default=None)
+    ap.add_argument("--records", default=None, help="also write the profiling records (JSON) here")
+    ap.add_argument("--from-records", default=None, help="compile from saved records (no GPU)")
     a = ap.parse_args()
     t0 = time.time()
-    recs = profile(corpus(a.quick), log=lambda s: print(s, flush=True))
+    if a.from_records:
+        with open(a.from_records) as f:
+            recs = json.load(f)
+        for r in recs:
+            r["block"] = tuple(r["block"])
+            r["latency"] = {int(k): v for k, v in r["latency"].items()}
+    else:
+        recs = profile(corpus(a.quick), log=lambda s: print(s, flush=True))
+        if a.records:
+            with open(a.records, "w") as f:
+                json.dump(recs, f)
     version = a.version or time.strftime("v1-%Y%m%d", time.gmtime())
     text = ("# Plan table for gfx950 (MI355X), compiled by profile_table.py from %d synthetic\n"
             "# profiling cases in %.0f s.  Format: see csrc/catalog.cpp.\n" % (len(recs), time.time() - t0))

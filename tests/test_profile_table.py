@@ -37,7 +37,10 @@ def test_geometric_mean_ranking_and_validity(tmp_path):
             _rec((128, 128), 8192, 0.31, 0.7, 1.3, {a: 4.0, b: 2.1})]
     text = pt.compile_table(recs, "vtest")
     lines = [ln for ln in text.splitlines() if ln.startswith("regime")]
-    assert len(lines) == 1  # both cases fall in one regime
+    # both cases fall in one regime; then the coarser regimes of the key
+    assert len(lines) == 3
+    assert lines[1].split(" : ")[0].split()[6:] == ["*", "*", "*"]
+    assert lines[2].split(" : ")[0].split()[4:] == ["*"] * 5
     names = {e["id"]: e["name"] for e in bsa.catalog()}
     ranking = lines[0].split(" : ")[1].split()
     gm_a, gm_b = math.sqrt(1.0 * 4.0), math.sqrt(2.0 * 2.1)
@@ -60,7 +63,9 @@ def test_geometric_mean_ranking_and_validity(tmp_path):
         pid, reg = bsa.select(8, 8192, 128, (128, 128), 0.3, 0.6, 1.2)
         assert reg == 0 and pid == a
         pid, reg = bsa.select(8, 8192, 128, (128, 128), 0.05, 0.6, 1.2)  # other density bucket
-        assert reg == -1 and pid == bsa.base_plan(8, 8192, 128, (128, 128))
+        assert reg == 1 and pid == a  # the coarser regime of the same request dimensions
+        pid, reg = bsa.select(8, 8192, 128, (64, 64), 0.3, 0.6, 1.2)  # key never profiled
+        assert reg == -1 and pid == bsa.base_plan(8, 8192, 128, (64, 64))
     finally:
         bsa.table_load(None)
 
@@ -73,7 +78,8 @@ def test_cases_split_by_key_and_buckets():
             _rec((128, 128), 8192, 0.3, 0.6, 1.0, {i128[3]: 1.0}, H=40),  # head-count bucket differs
             _rec((64, 64), 8192, 0.3, 0.6, 1.0, {i64[0]: 1.0})]       # key differs
     text = pt.compile_table(recs, "v2")
-    assert sum(ln.startswith("regime") for ln in text.splitlines()) == 5
+    fine = [ln for ln in text.splitlines() if ln.startswith("regime") and "*" not in ln]
+    assert len(fine) == 5
 
 
 def test_corpus_seeds_disjoint_from_workloads():
