@@ -118,3 +118,21 @@ def test_ablation_summary_metrics():
     assert s["A2_vs_A0_kernel_wins_ties_losses"] == [1, 1, 1]
     assert s["kernel_speedup_over_direct_gm"]["A2_table"] == pytest.approx((2.0 / 1.1 / 1.01) ** (1 / 3))
     assert s["cold_request_speedup_gm"]["A2_over_A1"] == pytest.approx((15 * (20 / 2.2) * 5) ** (1 / 3))
+
+
+def test_builtin_table_recompiles_from_its_records():
+    """The shipped table is exactly what the compiler makes of the shipped
+    profiling records (same catalog, same bounds, same rankings)."""
+    import json
+    import os
+    tables = os.path.join(os.path.dirname(pt.__file__), "tables")
+    with open(os.path.join(tables, "gfx950_v1_records.json")) as f:
+        recs = json.load(f)
+    for r in recs:
+        r["block"] = tuple(r["block"])
+        r["latency"] = {int(k): v for k, v in r["latency"].items()}
+    with open(os.path.join(tables, "gfx950_v1.txt")) as f:
+        shipped = [ln for ln in f.read().splitlines() if ln.startswith(("regime", "bounds", "catalog"))]
+    fresh = [ln for ln in pt.compile_table(recs, "x").splitlines()
+             if ln.startswith(("regime", "bounds", "catalog"))]
+    assert fresh == shipped
