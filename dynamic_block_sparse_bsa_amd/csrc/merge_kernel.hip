@@ -4,7 +4,7 @@
 // maxima are in log2 units (scores times log2(e)/sqrt(d)), so the weights are
 // exp2(m_p - m*).  A row whose partitions are all empty (l = 0) outputs zeros.
 //
-// One workgroup per (split query tile, 32 output columns), so even a few
+// One workgroup per (split query tile, 16 output columns), so even a few
 // split tiles spread over many CUs.  The per-row weights w_p / sum_p w_p l_p
 // are computed once per workgroup (one thread per row) into LDS; the threads
 // then stream the partial accumulators, four output columns per thread item,
@@ -17,6 +17,7 @@ namespace {
 
 constexpr int kMaxParts = 32;   // partitions whose weights are held in LDS
 constexpr int kMaxTq = 256;
+constexpr int kCols = 16;       // output columns per workgroup
 
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   __shared__ float wgt[kMaxParts][kMaxTq];
@@ -33,11 +34,13 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   // partitions go to LDS, further ones are recomputed while streaming
   float mstar = -INFINITY, inv = 0.0f;
   if (t < TQ) {
+#pragma unroll 4
     for (int p = 0; p < parts; ++p) {
       const size_t s = (size_t)(sb + p) * TQ + t;
       if (a.ws_l[s] > 0.0f) mstar = fmaxf(mstar, a.ws_m[s]);
     }
     float den = 0.0f;
+#pragma unroll 4
     for (int p = 0; p < parts; ++p) {
       const size_t s = (size_t)(sb + p) * TQ + t;
       const float l = a.ws_l[s];
@@ -50,14 +53,16 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   }
   __syncthreads();
   // (2) out[r][c..c+3] = sum_p wgt[p][r] * O_p[c..c+3][r], c in this
-  // workgroup's 32 columns
-  const int nitems = TQ * 8;
+  // workgroup's kCols columns; the partition loop is unrolled so several
+  // partitions' loads are in flight together
+  const int nitems = TQ * (kCols / 4);
   for (int item = t; item < nitems; item += 256) {
     const int r = item % TQ;
-    const int c = blockIdx.y * 32 + (item / TQ) * 4;
+    const int c = blockIdx.y * kCols + (item / TQ) * 4;
     const int row = qt * TQ + r;
     if (row >= a.N) continue;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
     for (int p = 0; p < parts; ++p) {
       float w;
       if (p < kMaxParts) {
@@ -90,8 +95,8 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
 
 hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s) {
   if (a.tq > kMaxTq) return hipErrorInvalidValue;
-  if (a.d % 32) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_merge, dim3(n_qtiles, a.d / 32), dim3(256), 0, s, a);
+  if (a.d % kCols) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_merge, dim3(n_qtiles, a.d / kCols), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -334,6 +334,8 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
   // pass 1: partition counts and workspace slots in query-tile order; the
   // tasks themselves (query-tile order) or their length histogram
   int32_t carry_t = 0, carry_s = 0;
+  RowTasks keep[4];  // a single chunk's rows and slot offset, reused by pass 2
+  int32_t keep_off_s = 0;
   for (int base = 0; base < nqt; base += 4096) {
     const int g0 = base + 4 * t;
     RowTasks r[4];
@@ -350,6 +352,9 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
     int32_t tot_t, tot_s;
     int32_t off_t = carry_t + block_scan(sum_t, lds, &tot_t);
     int32_t off_s = carry_s + block_scan(sum_s, lds, &tot_s);
+    keep_off_s = off_s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) keep[k] = r[k];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int g = g0 + k;
@@ -382,17 +387,23 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
   for (int base = 0; base < nqt; base += 4096) {
     const int g0 = base + 4 * t;
     RowTasks r[4];
-    int32_t sum_s = 0;
+    int32_t off_s, tot_s = 0;
+    if (nqt <= 4096) {  // one chunk: its rows are still in registers
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      r[k].p = 0;
-      if (g0 + k < nqt) {
-        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split);
-        sum_s += r[k].p > 1 ? r[k].p : 0;
+      for (int k = 0; k < 4; ++k) r[k] = keep[k];
+      off_s = keep_off_s;
+    } else {
+      int32_t sum_s = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        r[k].p = 0;
+        if (g0 + k < nqt) {
+          r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split);
+          sum_s += r[k].p > 1 ? r[k].p : 0;
+        }
       }
+      off_s = carry_s + block_scan(sum_s, lds, &tot_s);
     }
-    int32_t tot_s;
-    int32_t off_s = carry_s + block_scan(sum_s, lds, &tot_s);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (g0 + k >= nqt) break;
