@@ -125,6 +125,8 @@ MaskStats* pinned_stats() {
     if (hipHostMalloc((void**)&p, sizeof(MaskStats), hipHostMallocCoherent | hipHostMallocPortable) !=
         hipSuccess)
       p = nullptr;
+    else
+      std::memset(p, 0, sizeof(MaskStats));  // sequence numbers start at 1
   }
   return p;
 }
@@ -378,7 +380,9 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   HIP_TRY(pool_alloc(p->dev, sizeof(RowPartial) * (size_t)npart, &p->row_part));
   RowPartial* part = (RowPartial*)p->row_part.ptr;
   HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, part, s));
-  HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, host, s));
+  thread_local unsigned long long seq = 0;  // the host statistics buffer is per thread
+  ++seq;
+  HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, host, seq, s));
   // When a column array sized for every block is modest, the compaction is
   // queued before the statistics synchronization, so it overlaps the host's
   // wait and plan selection.
@@ -388,7 +392,20 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     HIP_TRY(pool_alloc(p->dev, cols_bound, &p->cols));
     HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
   }
-  HIP_TRY(hipStreamSynchronize(s));
+  // Wait for the statistics alone (the compaction may still run): spin on the
+  // sequence number the scan kernel stores last, checking the stream now and
+  // then so that a failed or finished stream ends the wait.
+  for (unsigned spin = 1;; ++spin) {
+    if (__atomic_load_n(&host->seq, __ATOMIC_ACQUIRE) == seq) break;
+    if ((spin & 255) == 0) {
+      const hipError_t q = hipStreamQuery(s);
+      if (q == hipSuccess) {
+        if (__atomic_load_n(&host->seq, __ATOMIC_ACQUIRE) == seq) break;
+        return fail(BSA_ERR_HIP, "mask statistics were not delivered");
+      }
+      if (q != hipErrorNotReady) return fail(BSA_ERR_HIP, "waiting for the mask statistics: %s", hipGetErrorString(q));
+    }
+  }
   std::memcpy(&p->stats, host, sizeof(MaskStats));
   const double total_blocks = (double)r.H * p->nqb * p->nkb;
   const double density = p->stats.nnz / total_blocks;
@@ -445,7 +462,7 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
                            ntc, (int32_t*)p->trow_cnt.ptr, nullptr, nullptr, nullptr, s));
     HIP_TRY(launch_scan((int32_t*)p->trow_cnt.ptr, (int32_t*)p->trow_ptr_buf.ptr, ntrows, nullptr, 0, nullptr,
-                        nullptr, s));
+                        nullptr, 0, s));
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
                            ntc, nullptr, (int32_t*)p->trow_ptr_buf.ptr, (int32_t*)p->tcol_buf.ptr,
                            (uint32_t*)p->tbits_buf.ptr, s));

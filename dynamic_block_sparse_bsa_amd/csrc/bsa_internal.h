@@ -29,6 +29,7 @@ struct MaskStats {
   unsigned int max_row_nnz;          // largest active count of a query-block row
   unsigned int empty_rows;           // query-block rows with no active block
   unsigned long long n_tasks;        // tasks written by the task builder
+  unsigned long long seq;            // host copy: request sequence number, written last
 };
 
 // Per-workgroup partial statistics of the row-count kernel.
@@ -84,7 +85,8 @@ hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int
 // Exclusive scan; with st non-null also completes the mask statistics (and
 // copies them to host_st, fine-grained host memory, when non-null).
 hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPartial* part,
-                       int32_t npart, MaskStats* st, MaskStats* host_st, hipStream_t s);
+                       int32_t npart, MaskStats* st, MaskStats* host_st, unsigned long long seq,
+                       hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
                           int32_t* cols, hipStream_t s);
 hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,

@@ -113,7 +113,8 @@ __device__ int32_t block_scan(int32_t v, int32_t* lds, int32_t* tot) {
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
                                                int32_t* __restrict__ out, int32_t n,
                                                const RowPartial* __restrict__ part, int32_t npart,
-                                               MaskStats* st, MaskStats* host_st) {
+                                               MaskStats* st, MaskStats* host_st,
+                                               unsigned long long seq) {
   __shared__ int32_t lds[32];
   const int t = threadIdx.x;
   int32_t carry = 0;
@@ -170,8 +171,18 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
       r.max_row_nnz = s_max[0];
       r.empty_rows = s_empty[0];
       r.n_tasks = 0;
+      r.seq = seq;
       *st = r;
-      if (host_st) *host_st = r;  // fine-grained host memory: no copy needed
+      if (host_st) {
+        // fine-grained host memory, read by the host while this stream runs
+        // on: the fields, then (system-scope release) the sequence number
+        host_st->nnz = r.nnz;
+        host_st->long_run = r.long_run;
+        host_st->max_row_nnz = r.max_row_nnz;
+        host_st->empty_rows = r.empty_rows;
+        host_st->n_tasks = 0;
+        __hip_atomic_store(&host_st->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
     }
   }
 }
@@ -430,8 +441,9 @@ hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int
 }
 
 hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPartial* part,
-                       int32_t npart, MaskStats* st, MaskStats* host_st, hipStream_t s) {
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, in, out, n, part, npart, st, host_st);
+                       int32_t npart, MaskStats* st, MaskStats* host_st, unsigned long long seq,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, in, out, n, part, npart, st, host_st, seq);
   return hipGetLastError();
 }
 
