@@ -59,10 +59,8 @@ struct AttnShape {
   static constexpr int KBYTES = TKV * D * 2;
   static constexpr int VBYTES = TKV * D * 2;
   // LDS stages of the K/V pipeline: three (two tiles in flight while one is
-  // computed) when three stages of a workgroup fit 48 KB (three workgroups
-  // per CU), or 96 KB for the 8-wave workgroups that run one per CU; else two.
-  static constexpr int NSTAGE =
-      (3 * (KBYTES + VBYTES) <= 48 * 1024 || (WAVES >= 8 && 3 * (KBYTES + VBYTES) <= 96 * 1024)) ? 3 : 2;
+  // computed) when three stages of a workgroup fit 48 KB, else two.
+  static constexpr int NSTAGE = (3 * (KBYTES + VBYTES) <= 48 * 1024) ? 3 : 2;
   static_assert(CPT >= 1, "tile too small for the workgroup");
   static_assert(TQ % 32 == 0 && TKV % 32 == 0 && D % 32 == 0, "shape");
 };
