@@ -202,6 +202,32 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
 
 }  // namespace
 
+// Per-device cache of HIP events (timing and non-timing), so that creating
+// and destroying a plan per request creates no events in steady state.
+namespace {
+std::mutex g_ev_mu;
+std::map<std::pair<int, bool>, std::vector<hipEvent_t>> g_ev_cache;
+
+hipError_t event_get(int dev, bool timing, hipEvent_t* e) {
+  {
+    std::lock_guard<std::mutex> lk(g_ev_mu);
+    auto& v = g_ev_cache[{dev, timing}];
+    if (!v.empty()) {
+      *e = v.back();
+      v.pop_back();
+      return hipSuccess;
+    }
+  }
+  return hipEventCreateWithFlags(e, timing ? hipEventDefault : hipEventDisableTiming);
+}
+
+void event_put(int dev, bool timing, hipEvent_t e) {
+  if (!e) return;
+  std::lock_guard<std::mutex> lk(g_ev_mu);
+  g_ev_cache[{dev, timing}].push_back(e);
+}
+}  // namespace
+
 struct bsa_plan {
   bsa_request req{};
   int dev = 0;
@@ -218,16 +244,16 @@ struct bsa_plan {
   const int32_t* trow_ptr = nullptr;
   const int32_t* tcol = nullptr;
   const uint32_t* tbits = nullptr;
-  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-  hipEvent_t done = nullptr;  // recorded after the plan's latest stream work (create or run)
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};  // timing events of bsa_run_timed
+  hipEvent_t done = nullptr;  // recorded after plan creation and after untimed runs
+  hipEvent_t last = nullptr;  // recorded after the plan's latest stream work (done or ev[2])
 
   ~bsa_plan() {
     for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &row_part, &cols, &trow_cnt, &trow_ptr_buf, &tcol_buf,
                       &tbits_buf, &parts, &slot_off, &tasks, &ws})
       pool_release(b);
-    for (auto& e : ev)
-      if (e) (void)hipEventDestroy(e);
-    if (done) (void)hipEventDestroy(done);
+    for (auto& e : ev) event_put(dev, true, e);
+    event_put(dev, false, done);
   }
 };
 
@@ -515,8 +541,9 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   in.run_coverage = runcov;
   in.row_skew = skew;
   in.host_select_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
-  HIP_TRY(hipEventCreateWithFlags(&p->done, hipEventDisableTiming));
+  HIP_TRY(event_get(p->dev, false, &p->done));
   HIP_TRY(hipEventRecord(p->done, s));
+  p->last = p->done;
   *out = p.release();
   return BSA_OK;
 }
@@ -562,7 +589,7 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   bsa_plan* mp = const_cast<bsa_plan*>(p);
   if (timed) {
     for (auto& ev : mp->ev)
-      if (!ev) HIP_TRY(hipEventCreate(&ev));
+      if (!ev) HIP_TRY(event_get(p->dev, true, &ev));
     HIP_TRY(hipEventRecord(mp->ev[0], s));
   }
   HIP_TRY(fn(a, (int)p->grid, s));
@@ -581,9 +608,13 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
     m.d = e.d;
     HIP_TRY(launch_merge(m, (int32_t)p->shape.nqt, s));
   }
-  HIP_TRY(hipEventRecord(mp->done, s));
+  if (!timed) {
+    HIP_TRY(hipEventRecord(mp->done, s));
+    mp->last = mp->done;
+  }
   if (timed) {
     HIP_TRY(hipEventRecord(mp->ev[2], s));
+    mp->last = mp->ev[2];
     HIP_TRY(hipEventSynchronize(mp->ev[2]));
     float t = 0;
     HIP_TRY(hipEventElapsedTime(&t, mp->ev[0], mp->ev[1]));
@@ -607,7 +638,7 @@ bsa_status bsa_plan_destroy(bsa_plan* p) {
   if (!p) return BSA_OK;
   // wait for the plan's latest stream work (its creation or last run) before
   // its device memory returns to the cache
-  hipError_t e = p->done ? hipEventSynchronize(p->done) : hipDeviceSynchronize();
+  hipError_t e = p->last ? hipEventSynchronize(p->last) : hipDeviceSynchronize();
   delete p;
   if (e != hipSuccess) return fail(BSA_ERR_HIP, "waiting for the plan's work: %s", hipGetErrorString(e));
   return BSA_OK;
