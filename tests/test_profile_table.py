@@ -118,6 +118,27 @@ def test_ablation_summary_metrics():
     assert s["A2_vs_A0_kernel_wins_ties_losses"] == [1, 1, 1]
     assert s["kernel_speedup_over_direct_gm"]["A2_table"] == pytest.approx((2.0 / 1.1 / 1.01) ** (1 / 3))
     assert s["cold_request_speedup_gm"]["A2_over_A1"] == pytest.approx((15 * (20 / 2.2) * 5) ** (1 / 3))
+    assert s["selection_regret"]["p99"] == pytest.approx(1.1)
+    assert "four_pass_speedup_gm" not in s  # no A1 repeats recorded
+
+
+def test_ablation_four_pass_and_organization():
+    from dynamic_block_sparse_bsa_amd import ablation
+    rows = [dict(k_a0=2.0, k_a2=1.0, k_best=1.0, a0_cold_ms=4.0, a1_cold_ms=40.0, a2_cold_ms=4.0,
+                 a0_warm_ms=2.0, a1_warm_ms=3.0, a2_warm_ms=1.0, k_o0=1.5, k_o2=0.9),
+            dict(k_a0=1.0, k_a2=1.0, k_best=1.0, a0_cold_ms=2.0, a1_cold_ms=20.0, a2_cold_ms=2.0,
+                 a0_warm_ms=1.0, a1_warm_ms=1.5, a2_warm_ms=1.0, k_o0=None, k_o2=1.0)]
+    s = ablation.summarize(rows)
+    # four passes: (cold + 3 warm) / 4 per variant
+    a2 = [(4 + 3) / 4, (2 + 3) / 4]
+    a1 = [(40 + 9) / 4, (20 + 4.5) / 4]
+    assert s["four_pass_speedup_gm"]["A2_over_A1"] == pytest.approx((a1[0] / a2[0] * a1[1] / a2[1]) ** 0.5)
+    assert s["warm_repeat_speedup_gm"]["A2_over_A1"] == pytest.approx((3.0 * 1.5) ** 0.5)
+    o = s["organization_at_fixed_mapping"]
+    assert o["cases"] == 1  # the case without a base organization is left out
+    assert o["O1_over_O0_gm"] == pytest.approx(1.5) and o["O2_over_O0_gm"] == pytest.approx(1.5 / 0.9)
+    assert o["O1_regret_vs_O2_gm"] == pytest.approx(1 / 0.9)
+    assert o["O1_vs_O0_wins_ties_losses"] == [1, 0, 0]
 
 
 def test_builtin_table_recompiles_from_its_records():
