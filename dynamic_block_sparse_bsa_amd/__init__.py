@@ -83,6 +83,9 @@ def _load():
                              ctypes.c_double, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.bsa_table_load.argtypes = [ctypes.c_char_p]
     L.bsa_base_plan.argtypes = [ctypes.POINTER(Request), ctypes.POINTER(i32)]
+    L.bsa_plan_cache_create.argtypes = [i32, i64, ctypes.POINTER(P)]
+    L.bsa_plan_cache_get.argtypes = [P, ctypes.POINTER(Request), P, ctypes.POINTER(P), ctypes.POINTER(i32)]
+    L.bsa_plan_cache_destroy.argtypes = [P]
     for f in ("bsa_table_version", "bsa_catalog_hash", "bsa_status_string", "bsa_last_error"):
         getattr(L, f).restype = ctypes.c_char_p
     L.bsa_status_string.argtypes = [i32]
@@ -90,7 +93,7 @@ def _load():
               "bsa_plan_get_info", "bsa_plan_export_tiles", "bsa_plan_export_csr",
               "bsa_plan_export_tasks",
               "bsa_catalog_get", "bsa_plan_eligible", "bsa_select", "bsa_table_load",
-              "bsa_base_plan"):
+              "bsa_base_plan", "bsa_plan_cache_create", "bsa_plan_cache_get", "bsa_plan_cache_destroy"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -116,10 +119,12 @@ def _stream(stream):
 
 
 class Plan:
-    """A prepared plan (owns device metadata until destroyed or collected)."""
+    """A prepared plan (owns device metadata until destroyed or collected;
+    a plan returned by a PlanCache belongs to the cache instead)."""
 
-    def __init__(self, handle, H, N, d, block):
+    def __init__(self, handle, H, N, d, block, owned=True):
         self._h = handle
+        self._owned = owned
         self.H, self.N, self.d, self.block = H, N, d, block
 
     @property
@@ -176,7 +181,8 @@ class Plan:
     def destroy(self):
         if self._h is not None:
             h, self._h = self._h, None
-            _check(_load().bsa_plan_destroy(h))
+            if self._owned:
+                _check(_load().bsa_plan_destroy(h))
 
     def __del__(self):
         try:
@@ -185,18 +191,54 @@ class Plan:
             pass
 
 
-def plan(mask, block, H, N, d, force_plan=-1, force_split=-1, workspace_limit=0, stream=None):
-    """Create a plan. mask: CUDA uint8 tensor [H, ceil(N/B_Q), ceil(N/B_KV)]."""
+def _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit):
     import torch
     nq, nk = -(-N // block[0]), -(-N // block[1])
     if not (isinstance(mask, torch.Tensor) and mask.is_cuda and mask.dtype == torch.uint8):
         raise BsaError("BSA_ERR_INVALID_ARG", "mask must be a CUDA uint8 tensor")
     if tuple(mask.shape) != (H, nq, nk) or not mask.is_contiguous():
         raise BsaError("BSA_ERR_INVALID_ARG", f"mask must be contiguous {(H, nq, nk)}, got {tuple(mask.shape)}")
-    req = _request(H, N, d, block, mask.data_ptr(), force_plan, force_split, workspace_limit)
+    return _request(H, N, d, block, mask.data_ptr(), force_plan, force_split, workspace_limit)
+
+
+def plan(mask, block, H, N, d, force_plan=-1, force_split=-1, workspace_limit=0, stream=None):
+    """Create a plan. mask: CUDA uint8 tensor [H, ceil(N/B_Q), ceil(N/B_KV)]."""
+    req = _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit)
     h = ctypes.c_void_p()
     _check(_load().bsa_plan_create(ctypes.byref(req), _stream(stream), ctypes.byref(h)))
     return Plan(h, H, N, d, block)
+
+
+class PlanCache:
+    """bsa_plan_cache: prepared plans reused for exact repeats of a request
+    (same geometry and options, byte-identical mask)."""
+
+    def __init__(self, capacity=4, max_mask_bytes=0):
+        h = ctypes.c_void_p()
+        _check(_load().bsa_plan_cache_create(int(capacity), int(max_mask_bytes), ctypes.byref(h)))
+        self._h = h
+
+    def get(self, mask, block, H, N, d, force_plan=-1, force_split=-1, workspace_limit=0, stream=None):
+        """(Plan, hit): the cached plan of an identical earlier request, or a new one."""
+        if self._h is None:
+            raise BsaError("BSA_ERR_INVALID_ARG", "cache was destroyed")
+        req = _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit)
+        h = ctypes.c_void_p()
+        hit = ctypes.c_int32(0)
+        _check(_load().bsa_plan_cache_get(self._h, ctypes.byref(req), _stream(stream), ctypes.byref(h),
+                                          ctypes.byref(hit)))
+        return Plan(h, H, N, d, block, owned=False), bool(hit.value)
+
+    def destroy(self):
+        if self._h is not None:
+            h, self._h = self._h, None
+            _check(_load().bsa_plan_cache_destroy(h))
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
 
 
 def _tensors(p, q, k, v, out):

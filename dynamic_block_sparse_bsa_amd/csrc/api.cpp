@@ -8,7 +8,9 @@
 // eligible plan of the regime's ranking (the key's base plan on a lookup
 // miss), derives only that plan's metadata from the block-CSR, binds the
 // temporary workspace and invokes the plan's kernels.
+#include <algorithm>
 #include <chrono>
+#include <new>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -129,6 +131,36 @@ MaskStats* pinned_stats() {
       std::memset(p, 0, sizeof(MaskStats));  // sequence numbers start at 1
   }
   return p;
+}
+
+CompareResult* pinned_compare() {
+  thread_local CompareResult* p = nullptr;
+  if (!p) {
+    if (hipHostMalloc((void**)&p, sizeof(CompareResult), hipHostMallocCoherent | hipHostMallocPortable) !=
+        hipSuccess)
+      p = nullptr;
+    else
+      std::memset(p, 0, sizeof(CompareResult));
+  }
+  return p;
+}
+
+// Spins until the GPU has stored `seq` into *flag (a system-scope release
+// after the record's other fields), checking the stream now and then so that
+// a failed or finished stream ends the wait.
+bsa_status wait_host_seq(const unsigned long long* flag, unsigned long long seq, hipStream_t s,
+                         const char* what) {
+  for (unsigned spin = 1;; ++spin) {
+    if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == seq) return BSA_OK;
+    if ((spin & 255) == 0) {
+      const hipError_t q = hipStreamQuery(s);
+      if (q == hipSuccess) {
+        if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) == seq) return BSA_OK;
+        return fail(BSA_ERR_HIP, "%s were not delivered", what);
+      }
+      if (q != hipErrorNotReady) return fail(BSA_ERR_HIP, "waiting for the %s: %s", what, hipGetErrorString(q));
+    }
+  }
 }
 
 int device_cus(int dev) {
@@ -284,6 +316,37 @@ bsa_status validate_request(const bsa_request* r) {
 
 }  // namespace
 
+// ---- plan cache (warm exact repeats) -------------------------------------------
+struct bsa_plan_cache {
+  struct Entry {
+    bsa_request key{};  // mask pointer cleared
+    int dev = 0;
+    DevBuf mask_copy;
+    int64_t bytes = 0;
+    hipEvent_t copied = nullptr;  // recorded after the mask copy
+    bsa_plan* plan = nullptr;
+    uint64_t last_use = 0;
+  };
+  int capacity = 4;
+  int64_t max_bytes = 0;
+  std::vector<Entry> entries;
+  std::map<int, DevBuf> flags;  // per device: int32[kMaxCompare], zero between checks
+  uint64_t tick = 0;
+  std::mutex mu;
+};
+
+namespace {
+
+bool same_request(const bsa_request& a, const bsa_request& b) {
+  return a.H == b.H && a.N == b.N && a.d == b.d && a.block_q == b.block_q && a.block_kv == b.block_kv &&
+         a.dtype == b.dtype && a.layout == b.layout && a.force_plan == b.force_plan &&
+         a.force_split == b.force_split && a.workspace_limit == b.workspace_limit;
+}
+
+void drop_entry(bsa_plan_cache::Entry& e);
+
+}  // namespace
+
 extern "C" {
 
 const char* bsa_status_string(int32_t s) {
@@ -419,18 +482,10 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
   }
   // Wait for the statistics alone (the compaction may still run): spin on the
-  // sequence number the scan kernel stores last, checking the stream now and
-  // then so that a failed or finished stream ends the wait.
-  for (unsigned spin = 1;; ++spin) {
-    if (__atomic_load_n(&host->seq, __ATOMIC_ACQUIRE) == seq) break;
-    if ((spin & 255) == 0) {
-      const hipError_t q = hipStreamQuery(s);
-      if (q == hipSuccess) {
-        if (__atomic_load_n(&host->seq, __ATOMIC_ACQUIRE) == seq) break;
-        return fail(BSA_ERR_HIP, "mask statistics were not delivered");
-      }
-      if (q != hipErrorNotReady) return fail(BSA_ERR_HIP, "waiting for the mask statistics: %s", hipGetErrorString(q));
-    }
+  // sequence number the scan kernel stores last.
+  {
+    const bsa_status ws = wait_host_seq(&host->seq, seq, s, "mask statistics");
+    if (ws != BSA_OK) return ws;
   }
   std::memcpy(&p->stats, host, sizeof(MaskStats));
   const double total_blocks = (double)r.H * p->nqb * p->nkb;
@@ -732,4 +787,131 @@ bsa_status bsa_plan_export_tasks(const bsa_plan* p, int32_t* head, int32_t* q_ti
   return BSA_OK;
 }
 
+bsa_status bsa_plan_cache_create(int32_t capacity, int64_t max_mask_bytes, bsa_plan_cache** out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARG, "NULL argument");
+  if (capacity < 1 || capacity > 64) return fail(BSA_ERR_INVALID_ARG, "capacity %d not in [1, 64]", capacity);
+  if (max_mask_bytes < 0) return fail(BSA_ERR_INVALID_ARG, "max_mask_bytes < 0");
+  bsa_plan_cache* c = new (std::nothrow) bsa_plan_cache();
+  if (!c) return fail(BSA_ERR_NO_MEMORY, "host allocation failed");
+  c->capacity = capacity;
+  c->max_bytes = max_mask_bytes;
+  *out = c;
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_cache_get(bsa_plan_cache* c, const bsa_request* req, void* stream, bsa_plan** out,
+                              int32_t* hit) {
+  if (!c || !out || !hit) return fail(BSA_ERR_INVALID_ARG, "NULL argument");
+  const bsa_status vs = validate_request(req);
+  if (vs != BSA_OK) return vs;
+  hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lk(c->mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  const int64_t bytes = (int64_t)req->H * cdiv(req->N, req->block_q) * cdiv(req->N, req->block_kv);
+  *hit = 0;
+  *out = nullptr;
+  // candidates: same request on this device, most recently used first
+  std::vector<int> cand;
+  for (int i = 0; i < (int)c->entries.size(); ++i)
+    if (c->entries[i].dev == dev && same_request(c->entries[i].key, *req)) cand.push_back(i);
+  std::sort(cand.begin(), cand.end(),
+            [&](int a, int b) { return c->entries[a].last_use > c->entries[b].last_use; });
+  if ((int)cand.size() > kMaxCompare) cand.resize(kMaxCompare);
+  if (!cand.empty()) {
+    CompareResult* host = pinned_compare();
+    if (!host) return fail(BSA_ERR_NO_MEMORY, "pinned host allocation failed");
+    DevBuf& fl = c->flags[dev];
+    if (!fl.ptr) {
+      HIP_TRY(pool_alloc(dev, sizeof(int32_t) * kMaxCompare, &fl));
+      HIP_TRY(hipMemset(fl.ptr, 0, sizeof(int32_t) * kMaxCompare));
+    }
+    CompareArgs a{};
+    a.mask = req->mask;
+    a.ncand = (int32_t)cand.size();
+    for (int k = 0; k < a.ncand; ++k) {
+      a.cand[k] = (const uint8_t*)c->entries[cand[k]].mask_copy.ptr;
+      HIP_TRY(hipStreamWaitEvent(s, c->entries[cand[k]].copied, 0));  // copy made on another stream
+    }
+    a.bytes = bytes;
+    a.flags = (int32_t*)fl.ptr;
+    thread_local unsigned long long seq = 0;  // the host record is per thread
+    ++seq;
+    HIP_TRY(launch_mask_compare(a, host, seq, s));
+    const bsa_status ws = wait_host_seq(&host->seq, seq, s, "mask comparison results");
+    if (ws != BSA_OK) return ws;
+    for (int k = 0; k < a.ncand; ++k) {
+      if (!host->differs[k]) {
+        bsa_plan_cache::Entry& e = c->entries[cand[k]];
+        e.last_use = ++c->tick;
+        *out = e.plan;
+        *hit = 1;
+        return BSA_OK;
+      }
+    }
+  }
+  // miss: plan, keep a copy of the mask, evict the least recently used
+  bsa_plan* p = nullptr;
+  const bsa_status st = bsa_plan_create(req, stream, &p);
+  if (st != BSA_OK) return st;
+  bsa_plan_cache::Entry e;
+  e.key = *req;
+  e.key.mask = nullptr;
+  e.dev = dev;
+  e.bytes = bytes;
+  e.plan = p;
+  e.last_use = ++c->tick;
+  hipError_t he = pool_alloc(dev, (size_t)bytes, &e.mask_copy);
+  if (he == hipSuccess) he = hipMemcpyAsync(e.mask_copy.ptr, req->mask, (size_t)bytes, hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess) he = event_get(dev, false, &e.copied);
+  if (he == hipSuccess) he = hipEventRecord(e.copied, s);
+  if (he != hipSuccess) {
+    drop_entry(e);
+    return fail(BSA_ERR_HIP, "caching the mask: %s", hipGetErrorString(he));
+  }
+  c->entries.push_back(e);
+  auto total = [&]() {
+    int64_t t = 0;
+    for (auto& x : c->entries) t += x.bytes;
+    return t;
+  };
+  while ((int)c->entries.size() > c->capacity || (c->max_bytes > 0 && total() > c->max_bytes && c->entries.size() > 1)) {
+    int lru = -1;
+    for (int i = 0; i < (int)c->entries.size(); ++i)
+      if (c->entries[i].plan != p && (lru < 0 || c->entries[i].last_use < c->entries[lru].last_use)) lru = i;
+    if (lru < 0) break;
+    drop_entry(c->entries[lru]);
+    c->entries.erase(c->entries.begin() + lru);
+  }
+  *out = p;
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_cache_destroy(bsa_plan_cache* c) {
+  if (!c) return BSA_OK;
+  {
+    std::lock_guard<std::mutex> lk(c->mu);
+    for (auto& e : c->entries) drop_entry(e);
+    c->entries.clear();
+    for (auto& kv : c->flags) pool_release(&kv.second);
+  }
+  delete c;
+  return BSA_OK;
+}
+
 }  // extern "C"
+
+namespace {
+// Destroys a cache entry's plan (after its latest stream work) and returns
+// its mask copy once the copy has completed.
+void drop_entry(bsa_plan_cache::Entry& e) {
+  if (e.plan) (void)bsa_plan_destroy(e.plan);
+  e.plan = nullptr;
+  if (e.copied) {
+    (void)hipEventSynchronize(e.copied);
+    event_put(e.dev, false, e.copied);
+    e.copied = nullptr;
+  }
+  pool_release(&e.mask_copy);
+}
+}  // namespace

@@ -32,6 +32,22 @@ struct MaskStats {
   unsigned long long seq;            // host copy: request sequence number, written last
 };
 
+// Exact-repeat check of the plan cache: which of up to kMaxCompare cached
+// masks differ from the request's mask.
+constexpr int kMaxCompare = 8;
+struct CompareArgs {
+  const uint8_t* mask;                  // request mask (device)
+  const uint8_t* cand[kMaxCompare];     // cached mask copies (device)
+  int32_t ncand;
+  int64_t bytes;
+  int32_t* flags;                       // device [kMaxCompare], zero on entry and on exit
+};
+// Host record of the check, written by the GPU into coherent host memory.
+struct CompareResult {
+  int32_t differs[kMaxCompare];
+  unsigned long long seq;               // written last
+};
+
 // Per-workgroup partial statistics of the row-count kernel.
 struct RowPartial {
   unsigned long long long_run;
@@ -87,6 +103,8 @@ hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int
 hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPartial* part,
                        int32_t npart, MaskStats* st, MaskStats* host_st, unsigned long long seq,
                        hipStream_t s);
+hipError_t launch_mask_compare(const CompareArgs& a, CompareResult* host, unsigned long long seq,
+                               hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
                           int32_t* cols, hipStream_t s);
 hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,

@@ -429,7 +429,55 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
   }
 }
 
+// Plan cache, exact-repeat check: flags[c] = 1 when the request mask differs
+// from cached copy c anywhere (grid-stride over 16-byte words when both
+// pointers allow, else bytes; blockIdx.y = candidate).  Every writer stores
+// the same value, so the race between writers is benign.
+__global__ __launch_bounds__(256) void k_mask_compare(const CompareArgs a) {
+  const int c = blockIdx.y;
+  const uint8_t* m = a.mask;
+  const uint8_t* o = a.cand[c];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  bool diff = false;
+  if (((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(o)) & 15) == 0) {
+    const int64_t words = a.bytes / 16;
+    const uint4* mw = reinterpret_cast<const uint4*>(m);
+    const uint4* ow = reinterpret_cast<const uint4*>(o);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += stride) {
+      const uint4 x = mw[i], y = ow[i];
+      diff |= (x.x != y.x) | (x.y != y.y) | (x.z != y.z) | (x.w != y.w);
+    }
+    for (int64_t i = words * 16 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.bytes; i += stride)
+      diff |= m[i] != o[i];
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.bytes; i += stride) diff |= m[i] != o[i];
+  }
+  if (diff) a.flags[c] = 1;
+}
+
+// Copies the flags to the host record (then the sequence number, system-scope
+// release) and clears them for the next check.
+__global__ __launch_bounds__(64) void k_compare_publish(int32_t* flags, int32_t ncand, CompareResult* host,
+                                                        unsigned long long seq) {
+  const int t = threadIdx.x;
+  if (t < kMaxCompare) {
+    host->differs[t] = t < ncand ? flags[t] : 1;
+    flags[t] = 0;
+  }
+  __syncthreads();
+  if (t == 0) __hip_atomic_store(&host->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 }  // namespace
+
+hipError_t launch_mask_compare(const CompareArgs& a, CompareResult* host, unsigned long long seq,
+                               hipStream_t s) {
+  if (a.ncand < 1 || a.ncand > kMaxCompare) return hipErrorInvalidValue;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((a.bytes + 4095) / 4096, 512));
+  hipLaunchKernelGGL(k_mask_compare, dim3((unsigned)blocks, (unsigned)a.ncand), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_compare_publish, dim3(1), dim3(64), 0, s, a.flags, a.ncand, host, seq);
+  return hipGetLastError();
+}
 
 int row_count_blocks(int32_t nrows) { return std::max(1, std::min((nrows + 3) / 4, 2048)); }
 

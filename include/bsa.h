@@ -73,8 +73,9 @@ typedef struct {
   int32_t reserved;
   int64_t workspace_limit; /* bytes of split-K workspace allowed; 0 = no limit */
   /* device, uint8 [H][ceil(N/B_Q)][ceil(N/B_KV)], nonzero = active.  Read
-   * only during bsa_plan_create (which synchronizes the stream once before
-   * returning); the caller may reuse it afterwards. */
+   * by kernels that bsa_plan_create queues on its stream: the caller may
+   * overwrite it with work ordered after them on that stream, or once that
+   * stream has been synchronized. */
   const uint8_t* mask;
 } bsa_request;
 
@@ -191,6 +192,33 @@ bsa_status bsa_select(const bsa_request* req, double density, double run_coverag
  * the eligible entry with the smallest tile.  Host only.  *plan_id receives
  * the catalog id, or -1 with BSA_ERR_UNSUPPORTED when no entry is eligible. */
 bsa_status bsa_base_plan(const bsa_request* req, int32_t* plan_id);
+
+/* Plan cache for warm exact repeats (paper section 7.4: repeats of a request
+ * reuse its prepared plan state instead of planning again).  A cache holds up
+ * to `capacity` prepared plans (1..64) together with a device copy of each
+ * plan's mask, at most `max_mask_bytes` of copies in total (0 = no limit),
+ * and evicts the least recently used.  Host object; the mask copies and
+ * plans live on the device that is current at bsa_plan_cache_get.  Errors:
+ * BSA_ERR_INVALID_ARG, BSA_ERR_NO_MEMORY. */
+typedef struct bsa_plan_cache bsa_plan_cache;
+bsa_status bsa_plan_cache_create(int32_t capacity, int64_t max_mask_bytes, bsa_plan_cache** out);
+
+/* Returns a prepared plan for `req`.  Cached plans of the same request
+ * (H, N, d, B, dtype, layout, force_plan, force_split, workspace_limit) are
+ * compared with req->mask byte for byte on the GPU (one compare kernel, the
+ * result read back through host-coherent memory); an identical one is
+ * returned with *hit = 1 and no planning work.  Otherwise a plan is created
+ * as by bsa_plan_create, the mask is copied (stream-ordered) into the cache
+ * and *hit = 0.  The returned plan belongs to the cache: it stays valid until
+ * a later bsa_plan_cache_get evicts it or the cache is destroyed, and must
+ * not be passed to bsa_plan_destroy.  A returned plan must not have a run in
+ * flight on another stream (one run per plan at a time).  Errors: those of
+ * bsa_plan_create. */
+bsa_status bsa_plan_cache_get(bsa_plan_cache* cache, const bsa_request* req, void* stream, bsa_plan** out,
+                              int32_t* hit);
+
+/* Destroys every cached plan (after their latest stream work) and the cache. */
+bsa_status bsa_plan_cache_destroy(bsa_plan_cache* cache);
 
 /* Load a versioned plan table (text artifact) replacing the built-in one.
  * BSA_ERR_TABLE if unreadable, malformed, or built for another architecture
