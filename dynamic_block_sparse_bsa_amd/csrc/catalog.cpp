@@ -57,9 +57,18 @@ struct Bounds {
   std::vector<double> H, N, density, runcov, skew;
 };
 
+// A threshold test on one regime feature (a decision-tree leaf is the
+// conjunction of the tests on its path).
+struct Cond {
+  int feature;  // 0 H, 1 N, 2 density, 3 run coverage, 4 row skew
+  bool less;    // true: x < v; false: x >= v
+  double v;
+};
+
 struct Regime {
   int bq, bkv, d;
   int hb, nb, db, rb, sb;  // bucket index per feature, -1 = any
+  std::vector<Cond> conds;  // rule regimes: every test must hold
   std::vector<int> ranking;
 };
 
@@ -133,7 +142,7 @@ bool eligible(const CatalogEntry& e, const bsa_request& r, int64_t ws_bytes, std
     return false;
   };
   if (r.dtype != BSA_DTYPE_BF16) return no("dtype");
-  if (r.layout != BSA_LAYOUT_HND) return no("layout");
+  if (r.layout != BSA_LAYOUT_HND && r.layout != BSA_LAYOUT_NHD) return no("layout");
   if (r.d != e.d) return no("head dim");
   // a wave owns 32 query rows, so a coarsened query tile needs B_Q >= 32
   DimMap mq = map_dim(r.block_q, e.tq, 32);
@@ -167,12 +176,16 @@ Selection lookup(const bsa_request& r, double density, double run_coverage, doub
   const int hb = bucket(t.bounds.H, r.H), nb = bucket(t.bounds.N, r.N);
   const int db = bucket(t.bounds.density, density), rb = bucket(t.bounds.runcov, run_coverage);
   const int sb = bucket(t.bounds.skew, row_skew);
+  const double x[5] = {(double)r.H, (double)r.N, density, run_coverage, row_skew};
   for (size_t i = 0; i < t.regimes.size(); ++i) {
     const Regime& g = t.regimes[i];
     if (g.bq != r.block_q || g.bkv != r.block_kv || g.d != r.d) continue;
     if ((g.hb >= 0 && g.hb != hb) || (g.nb >= 0 && g.nb != nb) || (g.db >= 0 && g.db != db) ||
         (g.rb >= 0 && g.rb != rb) || (g.sb >= 0 && g.sb != sb))
       continue;
+    bool ok = true;
+    for (const Cond& c : g.conds) ok = ok && (c.less ? x[c.feature] < c.v : x[c.feature] >= c.v);
+    if (!ok) continue;
     s.regime = (int)i;
     s.candidates = g.ranking;
     break;
@@ -190,7 +203,11 @@ Selection lookup(const bsa_request& r, double density, double run_coverage, doub
 //   bounds <H|N|density|run_coverage> v1 v2 ...     (bucket k: b[k-1] <= x < b[k])
 //   bounds row_skew v1 ...   (row skew = max row count * rows / active blocks)
 //   regime <B_Q> <B_KV> <d> <hb> <nb> <db> <rb> <sb> : <plan name> <plan name> ...
-// Lines starting with '#' are comments; '*' matches any bucket.
+//   rule <B_Q> <B_KV> <d> [<feature><op><value> ...] : <plan name> ...
+//       (a decision-tree leaf: feature in H N density run_coverage row_skew,
+//        op '<' or '>=', every test must hold; no tests = the whole key)
+// Lines starting with '#' are comments; '*' matches any bucket.  Regimes of
+// both kinds are tried in file order and the first match is taken.
 namespace {
 bsa_status parse_table(const std::string& text, Table* out, std::string* err) {
   Table t;
@@ -240,10 +257,12 @@ bsa_status parse_table(const std::string& text, Table* out, std::string* err) {
       else if (f == "run_coverage") t.bounds.runcov = v;
       else if (f == "row_skew") t.bounds.skew = v;
       else return fail("unknown feature " + f);
-    } else if (kw == "regime") {
+    } else if (kw == "regime" || kw == "rule") {
       Regime g;
+      const int nfield = kw == "regime" ? 8 : 3;
       std::string tok[8];
-      for (auto& s : tok) ls >> s;
+      for (int i = 0; i < nfield; ++i) ls >> tok[i];
+      for (int i = nfield; i < 8; ++i) tok[i] = "*";
       auto num = [&](const std::string& s, int* out) {
         if (s == "*") {
           *out = -1;
@@ -258,9 +277,31 @@ bsa_status parse_table(const std::string& text, Table* out, std::string* err) {
       int* outs[8] = {&g.bq, &g.bkv, &g.d, &g.hb, &g.nb, &g.db, &g.rb, &g.sb};
       for (int i = 0; i < 8; ++i)
         if (!num(tok[i], outs[i])) return fail("bad regime field '" + tok[i] + "'");
-      std::string colon;
-      ls >> colon;
-      if (colon != ":") return fail("expected ':'");
+      if (g.bq < 0 || g.bkv < 0 || g.d < 0) return fail("regime key must be explicit");
+      if (kw == "rule") {
+        static const char* feats[5] = {"H", "N", "density", "run_coverage", "row_skew"};
+        std::string c;
+        while (ls >> c && c != ":") {
+          const size_t lt = c.find('<'), ge = c.find(">=");
+          const bool less = lt != std::string::npos;
+          const size_t at = less ? lt : ge;
+          if (at == std::string::npos || at == 0) return fail("bad rule test '" + c + "'");
+          const std::string f = c.substr(0, at), v = c.substr(at + (less ? 1 : 2));
+          int fi = -1;
+          for (int k = 0; k < 5; ++k)
+            if (f == feats[k]) fi = k;
+          if (fi < 0) return fail("unknown feature " + f);
+          char* end = nullptr;
+          const double x = std::strtod(v.c_str(), &end);
+          if (v.empty() || *end) return fail("bad threshold '" + v + "'");
+          g.conds.push_back({fi, less, x});
+        }
+        if (c != ":") return fail("expected ':'");
+      } else {
+        std::string colon;
+        ls >> colon;
+        if (colon != ":") return fail("expected ':'");
+      }
       std::string nm;
       while (ls >> nm) {
         auto it = std::find(names.begin(), names.end(), nm);

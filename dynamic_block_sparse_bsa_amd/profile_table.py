@@ -60,13 +60,24 @@ def bucket(bounds, x):
     return k
 
 
-def corpus(quick=False):
+def corpus(quick=False, extra=False):
     """Profiling cases: (key, H, N, family, density target, seed).  Seeds start
-    at 900000, disjoint from the benchmark workloads' (1000*c, 5000 + 10*r)."""
+    at 900000 (base corpus) and 910000 (extra corpus), disjoint from the
+    benchmark workloads' (1000*c, 5000 + 10*r) and the held-out ablation
+    cases' (950000...).
+
+    The extra corpus adds sizes and densities between the base corpus's, so
+    that a decision tree over the regime features finds enough cases per
+    leaf."""
     keys = [((64, 64), 128), ((128, 128), 128), ((128, 32), 128), ((32, 128), 128), ((64, 64), 64)]
     if quick:
         sizes, dens = [(4, 8192), (2, 65536)], [0.1, 0.3]
         big, big_dens = [(24, 32768)], [0.1]
+    elif extra:
+        sizes = [(12, 12288), (16, 16384), (8, 20480), (6, 28672), (4, 40960), (20, 49152), (3, 57344),
+                 (2, 81920)]
+        dens = [0.025, 0.045, 0.07, 0.09, 0.12, 0.16, 0.22, 0.3, 0.38, 0.48]
+        big, big_dens = [], []
     else:
         sizes = [(8, 8192), (8, 16384), (8, 32768), (4, 75600), (4, 115200)]
         dens = [0.03, 0.06, 0.1, 0.14, 0.2, 0.28, 0.4, 0.5]
@@ -74,14 +85,14 @@ def corpus(quick=False):
         big, big_dens = [(24, 75600), (32, 115200)], [0.06, 0.14, 0.22]
     families = ["clustered", "window", "iid_mixed", "iid"]
     cases = []
-    seed = 900000
+    seed = 910000 if extra else 900000
     for block, d in keys:
         for grid, rhos in ((sizes, dens), (big, big_dens)):
             for H, N in grid:
                 if d == 64 and N > 32768:
                     continue
                 for i, rho in enumerate(rhos):
-                    fam = families[(i + N) % 4]
+                    fam = families[(i + N // 4096 + H) % 4] if extra else families[(i + N) % 4]
                     if fam == "window" and block[0] != block[1]:
                         fam = "clustered"
                     cases.append(dict(block=block, d=d, H=H, N=N, family=fam, rho=rho, seed=seed))
@@ -194,50 +205,215 @@ def profile(cases, reps=5, warmup=3, log=print):
     return records
 
 
-def compile_table(records, version):
-    """Two-stage regime partition and geometric-mean ranking."""
+def _ranking(bsa, key, rs):
+    """Plans valid on every case of rs ranked by geometric-mean latency (top
+    TOP), ending with the key's base plan; None when no plan is common."""
+    common = set.intersection(*[set(r["latency"]) for r in rs]) if rs else set()
+    if not common:
+        return None, None
+    gm = {pid: math.exp(sum(math.log(r["latency"][pid]) for r in rs) / len(rs)) for pid in common}
+    ranking = sorted(common, key=lambda pid: (gm[pid], pid))[:TOP]
+    base = bsa.base_plan(rs[0]["H"], rs[0]["N"], key[2], (key[0], key[1]))
+    if ranking[-1] != base:
+        ranking.append(base)  # every ranking ends with the key's base plan
+    return ranking, gm[ranking[0]]
+
+
+# ---- decision-tree partition of a key's cases -------------------------------
+# Section 5.1 of the Tessera paper allows the second-stage boundaries to be
+# thresholds learned by a decision tree whose leaves are the regimes, with the
+# depth chosen by cross-validation over corpus folds that keep masks of one
+# source together and at least 32 cases per leaf.  The split criterion here
+# is the quantity the table serves: a leaf picks the plan with the lowest
+# geometric-mean latency over its cases, and a split is taken when it lowers
+# the summed log selection regret (latency of the leaf's plan over the
+# case's fastest valid plan) of its cases.
+
+FEATURES = ("H", "N", "density", "run_coverage", "row_skew")
+MIN_LEAF = 32
+MAX_DEPTH = 4
+
+
+def fit_tree(rs, depth, min_leaf=None):
+    """Greedy regret-minimizing tree over FEATURES.  Returns nested dicts:
+    {"idx": case indices} for a leaf, plus "f", "thr", "lo", "hi" for a split
+    (lo: feature < thr, hi: feature >= thr)."""
+    import numpy as np
+    min_leaf = MIN_LEAF if min_leaf is None else min_leaf
+    pids = sorted(set().union(*[set(r["latency"]) for r in rs]))
+    L = np.full((len(rs), len(pids)), np.inf)
+    for i, r in enumerate(rs):
+        for j, pid in enumerate(pids):
+            if pid in r["latency"]:
+                L[i, j] = math.log(r["latency"][pid])
+    best = L.min(axis=1)
+    X = np.array([[float(r[f]) for f in FEATURES] for r in rs])
+
+    def leaf_cost(idx):
+        return float(L[idx].sum(axis=0).min() - best[idx].sum())
+
+    def best_split(idx):
+        n = len(idx)
+        found = (math.inf, None)
+        for f in range(len(FEATURES)):
+            order = idx[np.argsort(X[idx, f], kind="stable")]
+            xs = X[order, f]
+            fin = np.isfinite(L[order])
+            cs = np.cumsum(np.where(fin, L[order], 0.0), axis=0)
+            bad = np.cumsum(~fin, axis=0)
+            cb = np.cumsum(best[order])
+            for k in range(min_leaf, n - min_leaf + 1):
+                if xs[k - 1] == xs[k]:
+                    continue
+                left = np.where(bad[k - 1] == 0, cs[k - 1], np.inf).min() - cb[k - 1]
+                right = np.where(bad[-1] - bad[k - 1] == 0, cs[-1] - cs[k - 1], np.inf).min() - (cb[-1] - cb[k - 1])
+                if left + right < found[0]:
+                    found = (float(left + right), (f, float((xs[k - 1] + xs[k]) / 2)))
+        return found
+
+    def grow(idx, dep):
+        node = {"idx": idx}
+        if dep == 0 or len(idx) < 2 * min_leaf:
+            return node
+        c, split = best_split(idx)
+        if split is None or not c < leaf_cost(idx) - 1e-9:
+            return node
+        f, thr = split
+        node.update(f=f, thr=thr, lo=grow(idx[X[idx, f] < thr], dep - 1), hi=grow(idx[X[idx, f] >= thr], dep - 1))
+        return node
+
+    return grow(np.arange(len(rs)), depth)
+
+
+def tree_leaves(node, path=()):
+    """(tests, case indices) per leaf; a test is (feature name, op, threshold)."""
+    if "f" not in node:
+        return [(list(path), node["idx"])]
+    f, thr = FEATURES[node["f"]], node["thr"]
+    return tree_leaves(node["lo"], path + ((f, "<", thr),)) + tree_leaves(node["hi"], path + ((f, ">=", thr),))
+
+
+def compile_table(records, version, partition="intervals"):
+    """Two-stage regime partition and geometric-mean ranking.  partition:
+    "intervals" (the fixed BOUNDS buckets, then coarser buckets) or
+    ("tree", depth) (decision-tree leaves per request key)."""
     import dynamic_block_sparse_bsa_amd as bsa
     cat = bsa.catalog()
     names = {e["id"]: e["name"] for e in cat}
-    groups = {}
+    keyed = {}
     for r in records:
-        key = (r["block"][0], r["block"][1], r["d"])
-        reg = (bucket(BOUNDS["H"], r["H"]), bucket(BOUNDS["N"], r["N"]),
-               bucket(BOUNDS["density"], r["density"]), bucket(BOUNDS["run_coverage"], r["run_coverage"]),
-               bucket(BOUNDS["row_skew"], r["row_skew"]))
-        groups.setdefault(key, {}).setdefault(reg, []).append(r)
+        if r["latency"]:
+            keyed.setdefault((r["block"][0], r["block"][1], r["d"]), []).append(r)
     lines = [f"bsa-plan-table {version}", "arch gfx950", f"catalog {bsa.catalog_hash()}"]
+
+    def emit(key, head, rs):
+        ranking, best = _ranking(bsa, key, rs)
+        if ranking is None:
+            return
+        lines.append(f"# {len(rs)} cases; best GM {best:.4f} ms")
+        lines.append(" ".join([head[0], str(key[0]), str(key[1]), str(key[2])] + ([head[1]] if head[1] else [])
+                              + [":"] + [names[p] for p in ranking]))
+
+    if partition != "intervals":
+        depth = partition[1]
+        lines.append(f"# partition: decision tree per key, depth <= {depth}, >= {MIN_LEAF} cases per leaf")
+        for key in sorted(keyed):
+            rs = keyed[key]
+            for tests, idx in tree_leaves(fit_tree(rs, depth)):
+                emit(key, ("rule", " ".join(f"{f}{op}{thr!r}" for f, op, thr in tests)), [rs[i] for i in idx])
+            emit(key, ("regime", " ".join(["*"] * 5)), rs)
+        return "\n".join(lines) + "\n"
+
     for f in ("H", "N", "density", "run_coverage", "row_skew"):
         if BOUNDS[f]:
             lines.append(f"bounds {f} " + " ".join(repr(float(x)) for x in BOUNDS[f]))
-    def emit(key, fields, rs):
-        common = set.intersection(*[set(r["latency"]) for r in rs]) if rs else set()
-        if not common:
-            return
-        gm = {pid: math.exp(sum(math.log(r["latency"][pid]) for r in rs) / len(rs)) for pid in common}
-        ranking = sorted(common, key=lambda pid: (gm[pid], pid))[:TOP]
-        base = bsa.base_plan(rs[0]["H"], rs[0]["N"], key[2], (key[0], key[1]))
-        if ranking[-1] != base:
-            ranking.append(base)  # every ranking ends with the key's base plan
-        lines.append(f"# {len(rs)} cases; best GM {gm[ranking[0]]:.4f} ms")
-        lines.append("regime %d %d %d %s : %s" % (key[0], key[1], key[2], " ".join(fields),
-                                                  " ".join(names[p] for p in ranking)))
-
-    for key in sorted(groups):
+    for key in sorted(keyed):
+        groups = {}
+        for r in keyed[key]:
+            reg = (bucket(BOUNDS["H"], r["H"]), bucket(BOUNDS["N"], r["N"]),
+                   bucket(BOUNDS["density"], r["density"]), bucket(BOUNDS["run_coverage"], r["run_coverage"]),
+                   bucket(BOUNDS["row_skew"], r["row_skew"]))
+            groups.setdefault(reg, []).append(r)
         # regimes: request-dimension and mask-statistic buckets
-        for reg in sorted(groups[key]):
+        for reg in sorted(groups):
             hb = str(reg[0]) if BOUNDS["H"] else "*"
-            emit(key, [hb] + [str(x) for x in reg[1:]], groups[key][reg])
+            emit(key, ("regime", " ".join([hb] + [str(x) for x in reg[1:]])), groups[reg])
         # coarser regimes after them (the lookup takes the first match): the
         # same request-dimension buckets with any mask statistics, then any
         # request of the key; a request misses only for a key never profiled
         coarse = {}
-        for reg, rs in groups[key].items():
+        for reg, rs in groups.items():
             coarse.setdefault(reg[:2], []).extend(rs)
         for (h, n) in sorted(coarse):
-            emit(key, [str(h) if BOUNDS["H"] else "*", str(n), "*", "*", "*"], coarse[(h, n)])
-        emit(key, ["*"] * 5, [r for rs in groups[key].values() for r in rs])
+            emit(key, ("regime", " ".join([str(h) if BOUNDS["H"] else "*", str(n), "*", "*", "*"])),
+                 coarse[(h, n)])
+        emit(key, ("regime", " ".join(["*"] * 5)), keyed[key])
     return "\n".join(lines) + "\n"
+
+
+def table_rankings(text):
+    """Rankings (catalog ids) of a table's regimes in file order (the regime
+    index that bsa_select reports)."""
+    import dynamic_block_sparse_bsa_amd as bsa
+    ids = {e["name"]: e["id"] for e in bsa.catalog()}
+    return [[ids[n] for n in ln.split(":", 1)[1].split()] for ln in text.splitlines()
+            if ln.startswith(("regime ", "rule "))]
+
+
+def selection_regret(text, cases):
+    """Per case: latency of the plan the table selects (its regime's first
+    plan valid on the case, else the base plan) over the case's fastest
+    valid plan.  Uses the library's own lookup on the loaded table."""
+    import tempfile
+
+    import dynamic_block_sparse_bsa_amd as bsa
+    rankings = table_rankings(text)
+    with tempfile.NamedTemporaryFile("w", suffix=".txt", delete=False) as f:
+        f.write(text)
+        path = f.name
+    out = []
+    try:
+        bsa.table_load(path)
+        for r in cases:
+            lat = r["latency"]
+            if not lat:
+                continue
+            block, H, N, d = tuple(r["block"]), r["H"], r["N"], r["d"]
+            _, reg = bsa.select(H, N, d, block, r["density"], r["run_coverage"], r["row_skew"])
+            cand = (rankings[reg] if reg >= 0 else []) + [bsa.base_plan(H, N, d, block)]
+            sel = next((p for p in cand if p in lat), None)
+            out.append((lat[sel] if sel is not None else max(lat.values())) / min(lat.values()))
+    finally:
+        bsa.table_load(None)
+        os.unlink(path)
+    return out
+
+
+def cross_validate(records, partitions):
+    """Leave-one-source-out cross-validation: the mask generator family is
+    the source, so every fold holds out all masks of one generator.  Returns
+    {partition: GM selection regret over all held-out cases}."""
+    fams = sorted(set(r["family"] for r in records))
+    res = {}
+    for part in partitions:
+        regrets = []
+        for fam in fams:
+            train = [r for r in records if r["family"] != fam]
+            test = [r for r in records if r["family"] == fam]
+            regrets += selection_regret(compile_table(train, "cv", part), test)
+        res[part] = math.exp(sum(math.log(x) for x in regrets) / len(regrets))
+    return res
+
+
+def choose_partition(records, log=print):
+    """The fixed intervals or the tree depth with the lowest cross-validated
+    regret (ties go to the simpler partition)."""
+    parts = ["intervals"] + [("tree", dep) for dep in range(MAX_DEPTH + 1)]
+    cv = cross_validate(records, parts)
+    for p in parts:
+        log(f"cv {p}: GM regret {cv[p]:.4f}")
+    best = min(parts, key=lambda p: (round(cv[p], 4), parts.index(p)))
+    return best, cv
 
 
 def main():
@@ -246,24 +422,52 @@ def main():
     ap.add_argument("--quick", action="store_true", help="small corpus (smoke test of the tool)")
     ap.add_argument("--version", default=None)
     ap.add_argument("--records", default=None, help="also write the profiling records (JSON) here")
-    ap.add_argument("--from-records", default=None, help="compile from saved records (no GPU)")
+    ap.add_argument("--from-records", default=None, nargs="+",
+                    help="compile from saved records (no GPU); several files are concatenated")
+    ap.add_argument("--corpus", default="base", choices=["base", "extra", "all"],
+                    help="which synthetic corpus to profile")
+    ap.add_argument("--shard", default=None, help="i/n: profile every n-th case starting at i")
+    ap.add_argument("--partition", default="auto",
+                    help="intervals | tree:<depth> | auto (cross-validated choice)")
     a = ap.parse_args()
     t0 = time.time()
     if a.from_records:
-        with open(a.from_records) as f:
-            recs = json.load(f)
+        recs = []
+        for path in a.from_records:
+            with open(path) as f:
+                recs.extend(json.load(f))
         for r in recs:
             r["block"] = tuple(r["block"])
             r["latency"] = {int(k): v for k, v in r["latency"].items()}
     else:
-        recs = profile(corpus(a.quick), log=lambda s: print(s, flush=True))
+        cases = []
+        if a.corpus in ("base", "all"):
+            cases += corpus(a.quick)
+        if a.corpus in ("extra", "all"):
+            cases += corpus(a.quick, extra=True)
+        if a.shard:
+            i, n = (int(x) for x in a.shard.split("/"))
+            cases = cases[i::n]
+        recs = profile(cases, log=lambda s: print(s, flush=True))
         if a.records:
             with open(a.records, "w") as f:
                 json.dump(recs, f)
     version = a.version or time.strftime("v1-%Y%m%d", time.gmtime())
-    text = ("# Plan table for gfx950 (MI355X), compiled by profile_table.py from %d synthetic\n"
-            "# profiling cases in %.0f s.  Format: see csrc/catalog.cpp.\n" % (len(recs), time.time() - t0))
-    text += compile_table(recs, version)
+    cvtext = ""
+    if a.partition == "auto":
+        part, cv = choose_partition(recs, log=lambda s: print(s, flush=True))
+        cvtext = "".join("# leave-one-source-out GM regret, %s: %.4f\n"
+                         % ("fixed intervals" if p == "intervals" else f"tree of depth <= {p[1]}", v)
+                         for p, v in cv.items())
+    elif a.partition == "intervals":
+        part = "intervals"
+    else:
+        part = ("tree", int(a.partition.split(":")[1]))
+    how = ("compiled from saved records" if a.from_records
+           else "profiled and compiled in %.0f s" % (time.time() - t0))
+    text = ("# Plan table for gfx950 (MI355X): %d synthetic profiling cases, %s by\n"
+            "# profile_table.py.  Format: see csrc/catalog.cpp.\n" % (len(recs), how))
+    text += cvtext + compile_table(recs, version, part)
     with open(a.out, "w") as f:
         f.write(text)
     print(f"wrote {a.out}: {text.count(chr(10) + 'regime')} regimes", flush=True)

@@ -139,6 +139,21 @@ def test_ablation_four_pass_and_organization():
     assert o["O1_over_O0_gm"] == pytest.approx(1.5) and o["O2_over_O0_gm"] == pytest.approx(1.5 / 0.9)
     assert o["O1_regret_vs_O2_gm"] == pytest.approx(1 / 0.9)
     assert o["O1_vs_O0_wins_ties_losses"] == [1, 0, 0]
+    assert "plan_cache_repeat" not in s
+
+
+def test_ablation_plan_cache_repeats():
+    from dynamic_block_sparse_bsa_amd import ablation
+    rows = [dict(k_a0=2.0, k_a2=1.0, k_best=1.0, a0_cold_ms=4.0, a1_cold_ms=40.0, a2_cold_ms=4.0,
+                 a0_warm_ms=2.0, a2_warm_ms=1.0, a2_cached_ms=1.25),
+            dict(k_a0=1.0, k_a2=1.0, k_best=1.0, a0_cold_ms=2.0, a1_cold_ms=20.0, a2_cold_ms=3.0,
+                 a0_warm_ms=1.0, a2_warm_ms=1.0, a2_cached_ms=1.05),
+            dict(k_a0=1.0, k_a2=1.0, k_best=1.0, a0_cold_ms=2.0, a1_cold_ms=20.0, a2_cold_ms=2.0,
+                 a0_warm_ms=1.0, a2_warm_ms=1.0, a2_cached_ms=1.1)]
+    c = ablation.summarize(rows)["plan_cache_repeat"]
+    assert c["A2_over_A0_gm"] == pytest.approx((2.0 / 1.25 / 1.05 / 1.1) ** (1 / 3))
+    assert c["cold_over_cached_gm"] == pytest.approx((4.0 / 1.25 * 3.0 / 1.05 * 2.0 / 1.1) ** (1 / 3))
+    assert c["median_check_ms"] == pytest.approx(0.1)  # median of 0.25, 0.05, 0.1
 
 
 def test_builtin_table_recompiles_from_its_records():
@@ -153,7 +168,95 @@ def test_builtin_table_recompiles_from_its_records():
         r["block"] = tuple(r["block"])
         r["latency"] = {int(k): v for k, v in r["latency"].items()}
     with open(os.path.join(tables, "gfx950_v1.txt")) as f:
-        shipped = [ln for ln in f.read().splitlines() if ln.startswith(("regime", "bounds", "catalog"))]
-    fresh = [ln for ln in pt.compile_table(recs, "x").splitlines()
-             if ln.startswith(("regime", "bounds", "catalog"))]
+        text = f.read()
+    # the partition the shipped table was compiled with is the cross-validated choice
+    part, _ = pt.choose_partition(recs, log=lambda s: None)
+    if part == "intervals":
+        assert "\nrule " not in text
+    else:
+        assert f"depth <= {part[1]}," in text
+    keep = ("regime", "rule", "bounds", "catalog")
+    shipped = [ln for ln in text.splitlines() if ln.startswith(keep)]
+    fresh = [ln for ln in pt.compile_table(recs, "x", part).splitlines() if ln.startswith(keep)]
     assert fresh == shipped
+
+
+def _two_regime_records(threshold, n_per_family=40, fams=("clustered", "window", "iid_mixed", "iid")):
+    """Synthetic records of key (128, 128): below `threshold` density plan a
+    is fastest, above it plan b; densities spread evenly over [0.02, 0.5]."""
+    ids = _ids((128, 128))
+    a, b = ids[0], ids[3]
+    recs = []
+    for fi, fam in enumerate(fams):
+        for i in range(n_per_family):
+            dens = 0.02 + 0.48 * (i + fi / len(fams)) / n_per_family
+            lat = {a: 1.0, b: 1.3} if dens < threshold else {a: 1.4, b: 1.0}
+            r = _rec((128, 128), 8192, dens, 0.6, 1.2, lat)
+            r["family"] = fam
+            recs.append(r)
+    return recs, a, b
+
+
+def test_tree_learns_density_threshold(tmp_path):
+    recs, a, b = _two_regime_records(0.27)
+    tree = pt.fit_tree(recs, 2)
+    assert tree["f"] == pt.FEATURES.index("density")
+    below = max(r["density"] for r in recs if r["density"] < 0.27)
+    above = min(r["density"] for r in recs if r["density"] >= 0.27)
+    assert below < tree["thr"] < above
+    # both leaves are pure: no further split lowers the regret
+    assert "f" not in tree["lo"] and "f" not in tree["hi"]
+    leaves = pt.tree_leaves(tree)
+    assert [len(idx) for _, idx in leaves] == [sum(r["density"] < 0.27 for r in recs),
+                                               sum(r["density"] >= 0.27 for r in recs)]
+    assert pt.fit_tree(recs, 0).keys() == {"idx"}
+    # the compiled table holds one rule per leaf; the library's lookup routes by the threshold
+    text = pt.compile_table(recs, "vtree", ("tree", 2))
+    rules = [ln for ln in text.splitlines() if ln.startswith("rule ")]
+    assert len(rules) == 2 and "density<" in rules[0] and "density>=" in rules[1]
+    path = tmp_path / "tree.txt"
+    path.write_text(text)
+    bsa.table_load(str(path))
+    try:
+        assert bsa.select(8, 8192, 128, (128, 128), 0.1, 0.6, 1.2) == (a, 0)
+        assert bsa.select(8, 8192, 128, (128, 128), 0.4, 0.6, 1.2) == (b, 1)
+        assert pt.selection_regret(text, recs) == [1.0] * len(recs)
+    finally:
+        bsa.table_load(None)
+
+
+def test_tree_keeps_min_leaf_cases():
+    # 12 of 48 cases below the threshold: a leaf of them would hold fewer than 32 cases
+    recs, a, b = _two_regime_records(0.14, n_per_family=12)
+    assert sum(r["density"] < 0.14 for r in recs) < pt.MIN_LEAF
+    tree = pt.fit_tree(recs, 3)
+    for _, idx in pt.tree_leaves(tree):
+        assert len(idx) >= pt.MIN_LEAF or len(pt.tree_leaves(tree)) == 1
+    assert len(pt.tree_leaves(tree)) == 1  # 48 cases cannot make two leaves of 32
+
+
+def test_cross_validation_prefers_tree_off_the_fixed_bounds():
+    # 0.27 lies inside the fixed density bucket [0.2, 0.35): the intervals mix both regimes
+    recs, _, _ = _two_regime_records(0.27)
+    cv = pt.cross_validate(recs, ["intervals", ("tree", 0), ("tree", 1)])
+    assert cv[("tree", 1)] < cv["intervals"] and cv[("tree", 1)] < cv[("tree", 0)]
+    assert cv[("tree", 1)] < 1.01
+    part, _ = pt.choose_partition(recs, log=lambda s: None)
+    assert part[0] == "tree" and part[1] >= 1
+
+
+def test_leave_one_source_out_folds():
+    """Every fold holds out all cases of one generator family: a plan that is
+    fastest only on one family's masks cannot be learned for that family."""
+    ids = _ids((128, 128))
+    a, b = ids[0], ids[3]
+    recs = []
+    for fam in ("clustered", "window", "iid_mixed", "iid"):
+        for i in range(40):
+            lat = {a: 1.0, b: 2.0} if fam != "iid" else {a: 2.0, b: 1.0}
+            r = _rec((128, 128), 8192, 0.02 + 0.01 * i, 0.6, 1.2, lat)
+            r["family"] = fam
+            recs.append(r)
+    cv = pt.cross_validate(recs, [("tree", 2)])
+    # the iid fold trains on a-favoring families only: regret 2 on its 40 cases, 1 elsewhere
+    assert cv[("tree", 2)] == pytest.approx(2.0 ** (40 / 160))
