@@ -20,6 +20,8 @@ _lib = None
 
 BSA_DTYPE_BF16 = 1
 BSA_LAYOUT_HND = 0
+BSA_LAYOUT_NHD = 1
+_LAYOUTS = {"HND": BSA_LAYOUT_HND, "NHD": BSA_LAYOUT_NHD}
 
 
 class BsaError(RuntimeError):
@@ -33,7 +35,7 @@ class Request(ctypes.Structure):
                 ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32),
                 ("force_plan", ctypes.c_int32), ("force_split", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("workspace_limit", ctypes.c_int64),
+                ("batch", ctypes.c_int32), ("workspace_limit", ctypes.c_int64),
                 ("mask", ctypes.c_void_p)]
 
 
@@ -105,10 +107,24 @@ def _check(st):
         raise BsaError(L.bsa_status_string(st).decode(), L.bsa_last_error().decode())
 
 
-def _request(H, N, d, block, mask_ptr=None, force_plan=-1, force_split=-1, workspace_limit=0):
+def _layout(layout):
+    if layout not in _LAYOUTS:
+        raise BsaError("BSA_ERR_INVALID_ARG", f"layout must be one of {sorted(_LAYOUTS)}, got {layout!r}")
+    return _LAYOUTS[layout]
+
+
+def _request(H, N, d, block, mask_ptr=None, force_plan=-1, force_split=-1, workspace_limit=0, batch=1,
+             layout="HND"):
     return Request(H=H, N=N, d=d, block_q=block[0], block_kv=block[1], dtype=BSA_DTYPE_BF16,
-                   layout=BSA_LAYOUT_HND, force_plan=force_plan, force_split=force_split,
-                   reserved=0, workspace_limit=workspace_limit, mask=mask_ptr)
+                   layout=_layout(layout), force_plan=force_plan, force_split=force_split,
+                   batch=batch, workspace_limit=workspace_limit, mask=mask_ptr)
+
+
+def tensor_shapes(H, N, d, batch=1, layout="HND"):
+    """Accepted Q/K/V/O shapes: [batch][H][N][d] (HND) or [batch][N][H][d]
+    (NHD); with batch 1 the leading dimension may be left out."""
+    inner = (H, N, d) if _layout(layout) == BSA_LAYOUT_HND else (N, H, d)
+    return [(batch,) + inner] + ([inner] if batch == 1 else [])
 
 
 def _stream(stream):
@@ -122,10 +138,11 @@ class Plan:
     """A prepared plan (owns device metadata until destroyed or collected;
     a plan returned by a PlanCache belongs to the cache instead)."""
 
-    def __init__(self, handle, H, N, d, block, owned=True):
+    def __init__(self, handle, H, N, d, block, owned=True, batch=1, layout="HND"):
         self._h = handle
         self._owned = owned
         self.H, self.N, self.d, self.block = H, N, d, block
+        self.batch, self.layout = batch, layout
 
     @property
     def handle(self):
@@ -171,7 +188,7 @@ class Plan:
     def export_csr(self):
         import numpy as np
         info = self.info
-        nrows = self.H * (-(-self.N // self.block[0]))
+        nrows = self.batch * self.H * (-(-self.N // self.block[0]))
         rp = np.empty(nrows + 1, np.int32)
         cols = np.empty(max(1, info["nnz_blocks"]), np.int32)
         _check(_load().bsa_plan_export_csr(self.handle, rp.ctypes.data_as(ctypes.c_void_p),
@@ -191,22 +208,26 @@ class Plan:
             pass
 
 
-def _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit):
+def _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit, batch, layout):
     import torch
     nq, nk = -(-N // block[0]), -(-N // block[1])
     if not (isinstance(mask, torch.Tensor) and mask.is_cuda and mask.dtype == torch.uint8):
         raise BsaError("BSA_ERR_INVALID_ARG", "mask must be a CUDA uint8 tensor")
-    if tuple(mask.shape) != (H, nq, nk) or not mask.is_contiguous():
-        raise BsaError("BSA_ERR_INVALID_ARG", f"mask must be contiguous {(H, nq, nk)}, got {tuple(mask.shape)}")
-    return _request(H, N, d, block, mask.data_ptr(), force_plan, force_split, workspace_limit)
+    ok = [(batch * H, nq, nk), (batch, H, nq, nk)]
+    if tuple(mask.shape) not in ok or not mask.is_contiguous():
+        raise BsaError("BSA_ERR_INVALID_ARG", f"mask must be contiguous {ok[0]} or {ok[1]}, got {tuple(mask.shape)}")
+    return _request(H, N, d, block, mask.data_ptr(), force_plan, force_split, workspace_limit, batch, layout)
 
 
-def plan(mask, block, H, N, d, force_plan=-1, force_split=-1, workspace_limit=0, stream=None):
-    """Create a plan. mask: CUDA uint8 tensor [H, ceil(N/B_Q), ceil(N/B_KV)]."""
-    req = _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit)
+def plan(mask, block, H, N, d, force_plan=-1, force_split=-1, workspace_limit=0, stream=None, batch=1,
+         layout="HND"):
+    """Create a plan. mask: CUDA uint8 tensor [batch*H, ceil(N/B_Q), ceil(N/B_KV)]
+    (or with batch and head dimensions apart); layout "HND" or "NHD" for the
+    tensors the plan will run on."""
+    req = _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit, batch, layout)
     h = ctypes.c_void_p()
     _check(_load().bsa_plan_create(ctypes.byref(req), _stream(stream), ctypes.byref(h)))
-    return Plan(h, H, N, d, block)
+    return Plan(h, H, N, d, block, batch=batch, layout=layout)
 
 
 class PlanCache:
@@ -218,16 +239,17 @@ class PlanCache:
         _check(_load().bsa_plan_cache_create(int(capacity), int(max_mask_bytes), ctypes.byref(h)))
         self._h = h
 
-    def get(self, mask, block, H, N, d, force_plan=-1, force_split=-1, workspace_limit=0, stream=None):
+    def get(self, mask, block, H, N, d, force_plan=-1, force_split=-1, workspace_limit=0, stream=None, batch=1,
+            layout="HND"):
         """(Plan, hit): the cached plan of an identical earlier request, or a new one."""
         if self._h is None:
             raise BsaError("BSA_ERR_INVALID_ARG", "cache was destroyed")
-        req = _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit)
+        req = _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit, batch, layout)
         h = ctypes.c_void_p()
         hit = ctypes.c_int32(0)
         _check(_load().bsa_plan_cache_get(self._h, ctypes.byref(req), _stream(stream), ctypes.byref(h),
                                           ctypes.byref(hit)))
-        return Plan(h, H, N, d, block, owned=False), bool(hit.value)
+        return Plan(h, H, N, d, block, owned=False, batch=batch, layout=layout), bool(hit.value)
 
     def destroy(self):
         if self._h is not None:
@@ -243,16 +265,16 @@ class PlanCache:
 
 def _tensors(p, q, k, v, out):
     import torch
-    shape = (p.H, p.N, p.d)
+    shapes = tensor_shapes(p.H, p.N, p.d, p.batch, p.layout)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.bfloat16
-                and tuple(t.shape) == shape and t.is_contiguous()):
-            raise BsaError("BSA_ERR_INVALID_ARG", f"{name} must be a contiguous CUDA bf16 tensor {shape}")
+                and tuple(t.shape) in shapes and t.is_contiguous()):
+            raise BsaError("BSA_ERR_INVALID_ARG", f"{name} must be a contiguous CUDA bf16 tensor {shapes[-1]}")
     if out is None:
-        out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
-    elif not (out.is_cuda and out.dtype == torch.bfloat16 and tuple(out.shape) == shape
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    elif not (out.is_cuda and out.dtype == torch.bfloat16 and tuple(out.shape) in shapes
               and out.is_contiguous()):
-        raise BsaError("BSA_ERR_INVALID_ARG", f"out must be a contiguous CUDA bf16 tensor {shape}")
+        raise BsaError("BSA_ERR_INVALID_ARG", f"out must be a contiguous CUDA bf16 tensor {shapes[-1]}")
     return out
 
 
@@ -283,25 +305,25 @@ def catalog():
     return res
 
 
-def eligible(plan_id, H, N, d, block, workspace_limit=0):
-    r = _request(H, N, d, block, None, workspace_limit=workspace_limit)
+def eligible(plan_id, H, N, d, block, workspace_limit=0, batch=1, layout="HND"):
+    r = _request(H, N, d, block, None, workspace_limit=workspace_limit, batch=batch, layout=layout)
     out = ctypes.c_int32(0)
     _check(_load().bsa_plan_eligible(plan_id, ctypes.byref(r), ctypes.byref(out)))
     return bool(out.value)
 
 
-def select(H, N, d, block, density, run_coverage, row_skew=1.0):
+def select(H, N, d, block, density, run_coverage, row_skew=1.0, batch=1, layout="HND"):
     """Host-only regime lookup + ranked fallback: (plan_id, regime)."""
-    r = _request(H, N, d, block, None)
+    r = _request(H, N, d, block, None, batch=batch, layout=layout)
     pid, reg = ctypes.c_int32(-1), ctypes.c_int32(-1)
     _check(_load().bsa_select(ctypes.byref(r), density, run_coverage, row_skew, ctypes.byref(pid),
                               ctypes.byref(reg)))
     return pid.value, reg.value
 
 
-def base_plan(H, N, d, block):
+def base_plan(H, N, d, block, batch=1, layout="HND"):
     """Catalog id of the request key's base plan (host only)."""
-    r = _request(H, N, d, block, None)
+    r = _request(H, N, d, block, None, batch=batch, layout=layout)
     pid = ctypes.c_int32(-1)
     _check(_load().bsa_base_plan(ctypes.byref(r), ctypes.byref(pid)))
     return pid.value

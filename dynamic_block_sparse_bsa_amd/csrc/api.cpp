@@ -261,7 +261,8 @@ void event_put(int dev, bool timing, hipEvent_t e) {
 }  // namespace
 
 struct bsa_plan {
-  bsa_request req{};
+  bsa_request req{};    // batch folded into H (req.H = batch * heads, req.batch = 1)
+  int32_t heads = 0;    // heads per batch entry, as requested
   int dev = 0;
   int nqb = 0, nkb = 0;
   const CatalogEntry* entry = nullptr;
@@ -291,12 +292,31 @@ struct bsa_plan {
 
 namespace {
 
-bsa_status validate_request(const bsa_request* r) {
-  if (!r) return fail(BSA_ERR_INVALID_ARG, "request is NULL");
-  if (r->H < 1 || r->N < 1) return fail(BSA_ERR_INVALID_ARG, "H and N must be >= 1 (H=%d N=%d)", r->H, r->N);
-  if (!r->mask) return fail(BSA_ERR_INVALID_ARG, "mask pointer is NULL");
-  if (r->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_UNSUPPORTED, "dtype %d unsupported (bf16 only)", r->dtype);
-  if (r->layout != BSA_LAYOUT_HND) return fail(BSA_ERR_UNSUPPORTED, "layout %d unsupported", r->layout);
+// The request with its batch entries folded into the head count: every
+// (batch entry, head) pair is an independent head of the mask and the tasks.
+bsa_request folded(const bsa_request& r) {
+  bsa_request f = r;
+  if (r.batch > 1) f.H = (int32_t)((int64_t)r.H * r.batch);
+  f.batch = 1;
+  return f;
+}
+
+bsa_status validate_request(const bsa_request* rq) {
+  if (!rq) return fail(BSA_ERR_INVALID_ARG, "request is NULL");
+  if (rq->H < 1 || rq->N < 1) return fail(BSA_ERR_INVALID_ARG, "H and N must be >= 1 (H=%d N=%d)", rq->H, rq->N);
+  if (rq->batch < 0) return fail(BSA_ERR_INVALID_ARG, "batch %d < 0", rq->batch);
+  if ((int64_t)rq->H * std::max(rq->batch, 1) >= (int64_t(1) << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "batch * H too large");
+  if (!rq->mask) return fail(BSA_ERR_INVALID_ARG, "mask pointer is NULL");
+  if (rq->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_UNSUPPORTED, "dtype %d unsupported (bf16 only)", rq->dtype);
+  if (rq->layout != BSA_LAYOUT_HND && rq->layout != BSA_LAYOUT_NHD)
+    return fail(BSA_ERR_UNSUPPORTED, "layout %d unsupported", rq->layout);
+  // the kernels address one head's rows through 32-bit byte offsets
+  const int64_t row_bytes = (int64_t)rq->d * 2 * (rq->layout == BSA_LAYOUT_NHD ? rq->H : 1);
+  if ((int64_t)rq->N * row_bytes >= (int64_t(1) << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "N * row stride too large for layout %d", rq->layout);
+  const bsa_request fr = folded(*rq);
+  const bsa_request* r = &fr;
   if (r->d != 64 && r->d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim %d unsupported (64, 128)", r->d);
   if (!pow2(r->block_q) || r->block_q < 16 || r->block_q > 256)
     return fail(BSA_ERR_UNSUPPORTED, "block_q %d unsupported (power of two in [16, 256])", r->block_q);
@@ -338,8 +358,8 @@ struct bsa_plan_cache {
 namespace {
 
 bool same_request(const bsa_request& a, const bsa_request& b) {
-  return a.H == b.H && a.N == b.N && a.d == b.d && a.block_q == b.block_q && a.block_kv == b.block_kv &&
-         a.dtype == b.dtype && a.layout == b.layout && a.force_plan == b.force_plan &&
+  return a.H == b.H && std::max(a.batch, 1) == std::max(b.batch, 1) && a.N == b.N && a.d == b.d &&
+         a.block_q == b.block_q && a.block_kv == b.block_kv && a.dtype == b.dtype && a.layout == b.layout && a.force_plan == b.force_plan &&
          a.force_split == b.force_split && a.workspace_limit == b.workspace_limit;
 }
 
@@ -406,17 +426,18 @@ bsa_status bsa_plan_eligible(int32_t id, const bsa_request* req, int32_t* out) {
   if (!req || !out || id < 0 || id >= (int)catalog().size())
     return fail(BSA_ERR_INVALID_ARG, "bad arguments to bsa_plan_eligible");
   std::string why;
-  *out = eligible(catalog()[id], *req, -1, &why) ? 1 : 0;
+  *out = eligible(catalog()[id], folded(*req), -1, &why) ? 1 : 0;
   return BSA_OK;
 }
 
 bsa_status bsa_select(const bsa_request* req, double density, double run_coverage, double row_skew,
                       int32_t* plan_id, int32_t* regime) {
   if (!req || !plan_id || !regime) return fail(BSA_ERR_INVALID_ARG, "NULL argument to bsa_select");
-  Selection s = lookup(*req, density, run_coverage, row_skew);
+  const bsa_request fr = folded(*req);
+  Selection s = lookup(fr, density, run_coverage, row_skew);
   *regime = s.regime;
   for (int c : s.candidates) {
-    if (eligible(catalog()[c], *req, -1, nullptr)) {
+    if (eligible(catalog()[c], fr, -1, nullptr)) {
       *plan_id = c;
       return BSA_OK;
     }
@@ -427,7 +448,7 @@ bsa_status bsa_select(const bsa_request* req, double density, double run_coverag
 
 bsa_status bsa_base_plan(const bsa_request* req, int32_t* plan_id) {
   if (!req || !plan_id) return fail(BSA_ERR_INVALID_ARG, "NULL argument to bsa_base_plan");
-  *plan_id = base_plan(*req);
+  *plan_id = base_plan(folded(*req));
   if (*plan_id < 0)
     return fail(BSA_ERR_UNSUPPORTED, "no eligible base plan for B=(%d,%d) d=%d", req->block_q, req->block_kv,
                 req->d);
@@ -439,8 +460,12 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   *out = nullptr;
   bsa_status vs = validate_request(req);
   if (vs != BSA_OK) return vs;
+  const int32_t heads = req->H;
+  const bsa_request fr = folded(*req);
+  req = &fr;
   hipStream_t s = (hipStream_t)stream;
   std::unique_ptr<bsa_plan> p(new bsa_plan());
+  p->heads = heads;
   // On an error return, kernels already queued may still use the plan's
   // buffers: wait for the stream before they go back to the cache.
   struct DrainOnError {
@@ -632,6 +657,12 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   a.ws_m = ws;
   a.ws_l = ws ? ws + slots * e.tq : nullptr;
   a.ws_o = ws ? ws + 2 * slots * e.tq : nullptr;
+  // layout: HND = [batch*H][N][d] (one run of heads), NHD = [batch][N][H][d]
+  const bool nhd = r.layout == BSA_LAYOUT_NHD;
+  a.heads = nhd ? p->heads : r.H;
+  a.batch_stride = nhd ? (int64_t)r.N * p->heads * r.d : 0;
+  a.head_stride = nhd ? r.d : (int64_t)r.N * r.d;
+  a.row_stride = nhd ? p->heads * r.d : r.d;
   a.N = r.N;
   a.sub_log2 = ilog2(p->shape.mk.refine);
   a.bkv_log2 = ilog2(r.block_kv);
@@ -652,6 +683,10 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   if (p->shape.split > 0) {
     MergeArgs m{};
     m.o = (__bf16*)o;
+    m.heads = a.heads;
+    m.batch_stride = a.batch_stride;
+    m.head_stride = a.head_stride;
+    m.row_stride = a.row_stride;
     m.parts = (const int32_t*)p->parts.ptr;
     m.slot_base = (const int32_t*)p->slot_off.ptr;
     m.ws_m = a.ws_m;
@@ -808,7 +843,7 @@ bsa_status bsa_plan_cache_get(bsa_plan_cache* c, const bsa_request* req, void* s
   std::lock_guard<std::mutex> lk(c->mu);
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
-  const int64_t bytes = (int64_t)req->H * cdiv(req->N, req->block_q) * cdiv(req->N, req->block_kv);
+  const int64_t bytes = (int64_t)folded(*req).H * cdiv(req->N, req->block_q) * cdiv(req->N, req->block_kv);
   *hit = 0;
   *out = nullptr;
   // candidates: same request on this device, most recently used first

@@ -197,7 +197,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   const int n = lane & 31;   // query column within the wave (B operand / C column)
   const int hh = lane >> 5;  // lane half
   const int N = a.N;
-  const size_t head_off = (size_t)task.head * N * D;
+  const int bat = task.head / a.heads;
+  const size_t head_off = (size_t)bat * a.batch_stride + (size_t)(task.head - bat * a.heads) * a.head_stride;
+  const int RS = a.row_stride;  // elements between consecutive rows
   const int qrow = task.qtile * TQ + w * 32 + n;
 
   // ---- Q fragment: B operand of S^T = K Q^T, resident for the task -------
@@ -206,7 +208,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   bf16x8 qf[S::DK];
   {
     const bool ok = qrow < N;
-    const __bf16* qp = a.q + head_off + (size_t)(ok ? qrow : 0) * D + 8 * hh;
+    const __bf16* qp = a.q + head_off + (size_t)(ok ? qrow : 0) * RS + 8 * hh;
 #pragma unroll
     for (int c = 0; c < S::DK; ++c) {
       const bf16x8 raw = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
@@ -279,25 +281,27 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   for (int i = 0; i < LPW; ++i) {
     const int slot = (i * S::WAVES + w) * 64 + lane;
     const int row = slot / S::KCH;
-    goff[i] = row * (D * 2) + (((slot % S::KCH) ^ chunk_swz<D>(row)) << 4);
+    goff[i] = row * (RS * 2) + (((slot % S::KCH) ^ chunk_swz<D>(row)) << 4);
   }
   const char* const kh = reinterpret_cast<const char*>(a.k + head_off);
   const char* const vh = reinterpret_cast<const char*>(a.v + head_off);
-  // raw buffer descriptors over this head's K and V (bytes [0, N*D*2))
+  // raw buffer descriptors over this head's K and V rows (bytes
+  // [0, (N-1)*RS*2 + D*2); the host keeps N*RS*2 below 2^31)
   constexpr int kRsrcWord3 = 0x00020000;
+  const int range = (N - 1) * (RS * 2) + D * 2;
   const __amdgpu_buffer_rsrc_t krsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kh), (short)0, N * (D * 2), kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kh), (short)0, range, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t vrsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vh), (short)0, N * (D * 2), kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vh), (short)0, range, kRsrcWord3);
   auto issue = [&](int kv0, int buf) {
     unsigned char* kb = smem + buf * STAGE + w * 1024;
     unsigned char* vb = kb + S::KBYTES;
-    const char* kt = kh + (size_t)kv0 * (D * 2);
-    const char* vt = vh + (size_t)kv0 * (D * 2);
+    const char* kt = kh + (size_t)kv0 * (RS * 2);
+    const char* vt = vh + (size_t)kv0 * (RS * 2);
     if (kv0 + TKV <= N) {
       // buffer loads: head base in the descriptor, tile offset in an SGPR,
       // per-lane offset in a VGPR fixed for the task -- no address VALU work
-      const int soff = kv0 * (D * 2);
+      const int soff = kv0 * (RS * 2);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(kb + i * S::WAVES * 1024), 16, goff[i],
@@ -306,11 +310,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
                                                  soff, 0, 0);
       }
     } else {
-      const int last = (N - 1 - kv0) * (D * 2);  // offset of row N-1 within the tile
+      const int last = N - 1 - kv0;  // row N-1 within the tile
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        const int rowoff = goff[i] & ~(D * 2 - 1);
-        const int off = min(rowoff, last) + (goff[i] & (D * 2 - 1));
+        const int row = ((i * S::WAVES + w) * 64 + lane) / S::KCH;
+        const int off = min(row, last) * (RS * 2) + (goff[i] - row * (RS * 2));
         __builtin_amdgcn_global_load_lds(kt + off, (lds_void*)(kb + i * S::WAVES * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vt + off, (lds_void*)(vb + i * S::WAVES * 1024), 16, 0, 0);
       }
@@ -549,7 +553,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   if (task.slot < 0) {
     if (qrow < N) {
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-      __bf16* op = a.o + head_off + (size_t)qrow * D;
+      __bf16* op = a.o + head_off + (size_t)qrow * RS;
 #pragma unroll
       for (int b = 0; b < S::DB; ++b)
 #pragma unroll

@@ -68,6 +68,13 @@ struct AttnArgs {
   float* ws_m;            // [slot][T_Q]           running max (log2 units)
   float* ws_l;            // [slot][T_Q]           exponential sum
   float* ws_o;            // [slot][d][T_Q]        unnormalized accumulator
+  // Tensor layout (elements; d is contiguous): head g of the task list is
+  // head g % heads of batch entry g / heads, at g/heads * batch_stride +
+  // g%heads * head_stride, and consecutive rows are row_stride apart.
+  int64_t batch_stride;
+  int64_t head_stride;
+  int32_t heads;
+  int32_t row_stride;
   int32_t N;
   int32_t sub_log2;       // log2(refine_kv): K/V tiles per tile-list entry
   int32_t bkv_log2;       // log2(B_KV)
@@ -81,6 +88,10 @@ struct AttnArgs {
 
 struct MergeArgs {
   __bf16* o;
+  int64_t batch_stride;     // layout of O, as in AttnArgs
+  int64_t head_stride;
+  int32_t heads;
+  int32_t row_stride;
   const int32_t* parts;     // [n_qtiles] partitions per query tile
   const int32_t* slot_base; // [n_qtiles] first workspace slot of the query tile
   const float* ws_m;

@@ -26,6 +26,8 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   if (parts <= 1) return;
   const int h = g / a.n_qtiles_head;
   const int qt = g - h * a.n_qtiles_head;
+  const int bat = h / a.heads;
+  const size_t head_off = (size_t)bat * a.batch_stride + (size_t)(h - bat * a.heads) * a.head_stride;
   const int sb = a.slot_base[g];
   const int TQ = a.tq;
   const int D = a.d;
@@ -87,7 +89,8 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
     __bf16 ov[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc[i];
-    *reinterpret_cast<uint2*>(a.o + ((size_t)h * a.N + row) * D + c) = *reinterpret_cast<const uint2*>(ov);
+    *reinterpret_cast<uint2*>(a.o + head_off + (size_t)row * a.row_stride + c) =
+        *reinterpret_cast<const uint2*>(ov);
   }
 }
 

@@ -49,30 +49,37 @@ typedef enum {
 } bsa_status;
 
 enum { BSA_DTYPE_BF16 = 1 };
-enum { BSA_LAYOUT_HND = 0 }; /* [H][N][d], d contiguous, no padding */
+/* Q, K, V and O share one layout, d contiguous, no padding:
+ *   BSA_LAYOUT_HND  [batch][H][N][d]  (heads outermost within a batch entry)
+ *   BSA_LAYOUT_NHD  [batch][N][H][d]  (a token's heads adjacent; rows of one
+ *                                      head are H*d elements apart) */
+enum { BSA_LAYOUT_HND = 0, BSA_LAYOUT_NHD = 1 };
 
 /* Opaque prepared plan: owns the block-CSR, the selected plan's metadata
  * (tile lists, membership bits, tasks) and its split-K workspace. */
 typedef struct bsa_plan bsa_plan;
 
 /* A runtime request (paper section 4.4: R = <A, M, B, x>; section 3 and
- * section 5.1: batch, head count and sequence length).  Batch is folded into
- * H. */
+ * section 5.1: batch, head count and sequence length).  Every (batch entry,
+ * head) pair is an independent attention head: planning, the regime
+ * features and the task list see batch * H heads. */
 typedef struct {
-  int32_t H;         /* heads (times batch), >= 1                               */
+  int32_t H;         /* heads per batch entry, >= 1                             */
   int32_t N;         /* sequence length (queries = keys), >= 1                  */
   int32_t d;         /* head dimension: 64 or 128                               */
   int32_t block_q;   /* B_Q: 32, 64, 128 or 256                                 */
   int32_t block_kv;  /* B_KV: 16, 32, 64, 128 or 256                            */
   int32_t dtype;     /* BSA_DTYPE_BF16                                          */
-  int32_t layout;    /* BSA_LAYOUT_HND                                          */
+  int32_t layout;    /* BSA_LAYOUT_HND or BSA_LAYOUT_NHD; NHD needs
+                        N * H * d * 2 < 2^31 bytes (BSA_ERR_UNSUPPORTED)      */
   int32_t force_plan;  /* -1: regime table selection; >= 0: that catalog entry
                           (must be eligible, else BSA_ERR_UNSUPPORTED)          */
   int32_t force_split; /* -1: the plan's own split rule; 0: never split;
                           k > 0: at most k K/V items per task                   */
-  int32_t reserved;
+  int32_t batch;       /* batch entries, 0 or 1 = one                          */
   int64_t workspace_limit; /* bytes of split-K workspace allowed; 0 = no limit */
-  /* device, uint8 [H][ceil(N/B_Q)][ceil(N/B_KV)], nonzero = active.  Read
+  /* device, uint8 [batch][H][ceil(N/B_Q)][ceil(N/B_KV)], nonzero = active
+   * (the same for both layouts).  Read
    * by kernels that bsa_plan_create queues on its stream: the caller may
    * overwrite it with work ordered after them on that stream, or once that
    * stream has been synchronized. */
@@ -121,8 +128,8 @@ typedef struct {
 bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out);
 
 /* Run a prepared plan: O = BSA(Q, K, V).  Q, K, V, O are device bf16
- * [H][N][d] buffers (layout BSA_LAYOUT_HND); O is fully written (zeros for
- * empty rows).  Stream-ordered and asynchronous.  One run per plan may be in
+ * buffers of batch * H * N * d elements in the request's layout; O is fully
+ * written (zeros for empty rows).  Stream-ordered and asynchronous.  One run per plan may be in
  * flight at a time (the split-K workspace is per plan).  Q/K/V may alias each
  * other; O must not alias Q, K or V. */
 bsa_status bsa_run(const bsa_plan* plan, const void* q, const void* k, const void* v, void* o,

@@ -111,3 +111,76 @@ def test_table_load_rejects_bad_tables(tmp_path):
     finally:
         bsa.table_load(None)
     assert bsa.table_version() != "test1"
+
+
+def test_table_rules_parse_and_route(tmp_path):
+    """Decision-tree leaves in the table text: threshold tests on the regime
+    features, every test of a rule must hold, first match in file order."""
+    names = {e["id"]: e["name"] for e in bsa.catalog()}
+    ids = [e["id"] for e in bsa.catalog() if bsa.eligible(e["id"], 8, 8192, 128, (64, 64))]
+    a, b, c = ids[0], ids[1], ids[2]
+    head = f"bsa-plan-table vrules\narch gfx950\ncatalog {bsa.catalog_hash()}\n"
+    text = head + (f"rule 64 64 128 N<20000 density<0.25 : {names[a]}\n"
+                   f"rule 64 64 128 N<20000 density>=0.25 : {names[b]}\n"
+                   f"rule 64 64 128 H>=16 row_skew>=2.5 : {names[c]}\n")
+    p = tmp_path / "rules.txt"
+    p.write_text(text)
+    bsa.table_load(str(p))
+    try:
+        assert bsa.select(8, 8192, 128, (64, 64), 0.1, 0.5, 1.0) == (a, 0)
+        assert bsa.select(8, 8192, 128, (64, 64), 0.25, 0.5, 1.0) == (b, 1)
+        assert bsa.select(32, 40000, 128, (64, 64), 0.25, 0.5, 3.0) == (c, 2)
+        # no rule matches: the key's base plan, regime -1
+        assert bsa.select(8, 40000, 128, (64, 64), 0.25, 0.5, 3.0) == (bsa.base_plan(8, 40000, 128, (64, 64)), -1)
+    finally:
+        bsa.table_load(None)
+    for bad in (f"rule 64 64 128 density<<0.2 : {names[a]}\n", f"rule 64 64 128 depth<3 : {names[a]}\n",
+                f"rule 64 64 128 density=0.2 : {names[a]}\n", f"rule 64 64 128 density<0.2 {names[a]}\n",
+                f"rule 64 * 128 : {names[a]}\n"):
+        p.write_text(head + bad)
+        with pytest.raises(bsa.BsaError):
+            bsa.table_load(str(p))
+    assert bsa.table_version() != "vrules"
+
+
+def _create_status(**kw):
+    """bsa_plan_create on a request that host-side validation must reject
+    (the mask pointer is never dereferenced)."""
+    import ctypes
+    args = dict(H=4, N=1024, d=128, block=(64, 64), mask_ptr=16, batch=1, layout="HND")
+    args.update(kw)
+    req = bsa._request(args["H"], args["N"], args["d"], args["block"], args["mask_ptr"], batch=args["batch"],
+                       layout=args["layout"])
+    if "raw_layout" in kw:
+        req.layout = kw["raw_layout"]
+    h = ctypes.c_void_p()
+    L = bsa._load()
+    st = L.bsa_plan_create(ctypes.byref(req), None, ctypes.byref(h))
+    return L.bsa_status_string(st).decode()
+
+
+def test_layout_and_batch_validation():
+    assert _create_status(raw_layout=2) == "BSA_ERR_UNSUPPORTED"
+    assert _create_status(batch=-1) == "BSA_ERR_INVALID_ARG"
+    assert _create_status(H=1 << 16, batch=1 << 15) == "BSA_ERR_UNSUPPORTED"  # batch * H >= 2^31
+    # NHD rows of one head are H*d elements apart: N * H * d * 2 bytes must stay below 2^31
+    assert _create_status(H=64, N=131072, layout="NHD") == "BSA_ERR_UNSUPPORTED"
+    assert _create_status(mask_ptr=None, layout="NHD") == "BSA_ERR_INVALID_ARG"
+    with pytest.raises(bsa.BsaError):
+        bsa.tensor_shapes(4, 1024, 128, layout="HDN")
+
+
+def test_batch_folds_into_heads_for_selection():
+    """Every (batch entry, head) pair is one head of the request: the regime
+    lookup and eligibility see batch * H heads, for either layout."""
+    for block in ((64, 64), (128, 128)):
+        for dens in (0.05, 0.3):
+            want = bsa.select(32, 75600, 128, block, dens, 0.5, 1.5)
+            assert bsa.select(8, 75600, 128, block, dens, 0.5, 1.5, batch=4) == want
+            assert bsa.select(8, 75600, 128, block, dens, 0.5, 1.5, batch=4, layout="NHD") == want
+    assert bsa.base_plan(2, 4096, 64, (64, 64), batch=3) == bsa.base_plan(6, 4096, 64, (64, 64))
+    ids = [e["id"] for e in bsa.catalog()]
+    assert [bsa.eligible(i, 4, 2048, 128, (64, 64), layout="NHD") for i in ids] == \
+        [bsa.eligible(i, 4, 2048, 128, (64, 64)) for i in ids]
+    assert bsa.tensor_shapes(4, 100, 64, batch=2, layout="NHD") == [(2, 100, 4, 64)]
+    assert bsa.tensor_shapes(4, 100, 64) == [(1, 4, 100, 64), (4, 100, 64)]
