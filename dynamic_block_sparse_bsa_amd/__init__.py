@@ -88,6 +88,7 @@ def _load():
     L.bsa_plan_cache_create.argtypes = [i32, i64, ctypes.POINTER(P)]
     L.bsa_plan_cache_get.argtypes = [P, ctypes.POINTER(Request), P, ctypes.POINTER(P), ctypes.POINTER(i32)]
     L.bsa_plan_cache_destroy.argtypes = [P]
+    L.bsa_plan_cache_run.argtypes = [P, ctypes.POINTER(Request), P, P, P, P, P, ctypes.POINTER(i32)]
     for f in ("bsa_table_version", "bsa_catalog_hash", "bsa_status_string", "bsa_last_error"):
         getattr(L, f).restype = ctypes.c_char_p
     L.bsa_status_string.argtypes = [i32]
@@ -95,7 +96,8 @@ def _load():
               "bsa_plan_get_info", "bsa_plan_export_tiles", "bsa_plan_export_csr",
               "bsa_plan_export_tasks",
               "bsa_catalog_get", "bsa_plan_eligible", "bsa_select", "bsa_table_load",
-              "bsa_base_plan", "bsa_plan_cache_create", "bsa_plan_cache_get", "bsa_plan_cache_destroy"):
+              "bsa_base_plan", "bsa_plan_cache_create", "bsa_plan_cache_get", "bsa_plan_cache_destroy",
+              "bsa_plan_cache_run"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -250,6 +252,21 @@ class PlanCache:
         _check(_load().bsa_plan_cache_get(self._h, ctypes.byref(req), _stream(stream), ctypes.byref(h),
                                           ctypes.byref(hit)))
         return Plan(h, H, N, d, block, owned=False, batch=batch, layout=layout), bool(hit.value)
+
+    def run(self, mask, block, H, N, d, q, k, v, out=None, force_plan=-1, force_split=-1, workspace_limit=0,
+            stream=None, batch=1, layout="HND"):
+        """(out, hit): O = BSA(Q, K, V) for the request through the cache, the
+        repeat check overlapped with the speculative run of the most recently
+        used matching-geometry plan (bsa_plan_cache_run)."""
+        import types
+        if self._h is None:
+            raise BsaError("BSA_ERR_INVALID_ARG", "cache was destroyed")
+        req = _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit, batch, layout)
+        out = _tensors(types.SimpleNamespace(H=H, N=N, d=d, batch=batch, layout=layout), q, k, v, out)
+        hit = ctypes.c_int32(0)
+        _check(_load().bsa_plan_cache_run(self._h, ctypes.byref(req), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), _stream(stream), ctypes.byref(hit)))
+        return out, bool(hit.value)
 
     def destroy(self):
         if self._h is not None:

@@ -345,6 +345,7 @@ struct bsa_plan_cache {
     int64_t bytes = 0;
     hipEvent_t copied = nullptr;  // recorded after the mask copy
     bsa_plan* plan = nullptr;
+    DevBuf guard;  // task-count word of this plan's speculative runs
     uint64_t last_use = 0;
   };
   int capacity = 4;
@@ -364,6 +365,127 @@ bool same_request(const bsa_request& a, const bsa_request& b) {
 }
 
 void drop_entry(bsa_plan_cache::Entry& e);
+
+struct RunIO {
+  const void *q, *k, *v;
+  void* o;
+};
+
+}  // namespace
+
+static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, const void* v, void* o,
+                           hipStream_t s, bool timed, float* attn_ms, float* merge_ms,
+                           const unsigned long long* guard);
+
+namespace {
+
+// Looks the request up in the cache (candidates: same request on this device,
+// most recently used first, compared with the request mask on the GPU) and
+// returns a cached plan on an exact repeat, else plans, caches and returns a
+// new one.  With io: also runs the returned plan on io.  The most recently
+// used candidate then runs speculatively right behind the comparison, guarded
+// by its verdict, so the host's wait for the verdict overlaps that run.
+bsa_status cache_acquire(bsa_plan_cache* c, const bsa_request* req, hipStream_t s, const RunIO* io,
+                         bsa_plan** out, int32_t* hit) {
+  if (!c || !out || !hit) return fail(BSA_ERR_INVALID_ARG, "NULL argument");
+  const bsa_status vs = validate_request(req);
+  if (vs != BSA_OK) return vs;
+  if (io && (!io->q || !io->k || !io->v || !io->o)) return fail(BSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  std::lock_guard<std::mutex> lk(c->mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  const int64_t bytes = (int64_t)folded(*req).H * cdiv(req->N, req->block_q) * cdiv(req->N, req->block_kv);
+  *hit = 0;
+  *out = nullptr;
+  std::vector<int> cand;
+  for (int i = 0; i < (int)c->entries.size(); ++i)
+    if (c->entries[i].dev == dev && same_request(c->entries[i].key, *req)) cand.push_back(i);
+  std::sort(cand.begin(), cand.end(),
+            [&](int a, int b) { return c->entries[a].last_use > c->entries[b].last_use; });
+  if ((int)cand.size() > kMaxCompare) cand.resize(kMaxCompare);
+  if (!cand.empty()) {
+    CompareResult* host = pinned_compare();
+    if (!host) return fail(BSA_ERR_NO_MEMORY, "pinned host allocation failed");
+    DevBuf& fl = c->flags[dev];
+    if (!fl.ptr) {
+      HIP_TRY(pool_alloc(dev, sizeof(int32_t) * kMaxCompare, &fl));
+      HIP_TRY(hipMemset(fl.ptr, 0, sizeof(int32_t) * kMaxCompare));
+    }
+    CompareArgs a{};
+    a.mask = req->mask;
+    a.ncand = (int32_t)cand.size();
+    for (int k = 0; k < a.ncand; ++k) {
+      a.cand[k] = (const uint8_t*)c->entries[cand[k]].mask_copy.ptr;
+      HIP_TRY(hipStreamWaitEvent(s, c->entries[cand[k]].copied, 0));  // copy made on another stream
+    }
+    a.bytes = bytes;
+    a.flags = (int32_t*)fl.ptr;
+    // the guard word belongs to the speculated plan, so a run of it still
+    // queued on another stream never sees another request's verdict
+    bsa_plan* spec = c->entries[cand[0]].plan;
+    if (io) {
+      a.spec_ntasks = &((const MaskStats*)spec->stats_dev.ptr)->n_tasks;
+      a.guard = (unsigned long long*)c->entries[cand[0]].guard.ptr;
+    }
+    thread_local unsigned long long seq = 0;  // the host record is per thread
+    ++seq;
+    HIP_TRY(launch_mask_compare(a, host, seq, s));
+    if (io) {
+      const bsa_status rs = run_impl(spec, io->q, io->k, io->v, io->o, s, false, nullptr, nullptr, a.guard);
+      if (rs != BSA_OK) return rs;
+    }
+    const bsa_status ws = wait_host_seq(&host->seq, seq, s, "mask comparison results");
+    if (ws != BSA_OK) return ws;
+    for (int k = 0; k < a.ncand; ++k) {
+      if (!host->differs[k]) {
+        bsa_plan_cache::Entry& e = c->entries[cand[k]];
+        e.last_use = ++c->tick;
+        *out = e.plan;
+        *hit = 1;
+        if (io && k > 0) return run_impl(e.plan, io->q, io->k, io->v, io->o, s, false, nullptr, nullptr, nullptr);
+        return BSA_OK;
+      }
+    }
+  }
+  // miss: plan, keep a copy of the mask, evict the least recently used
+  bsa_plan* p = nullptr;
+  const bsa_status st = bsa_plan_create(req, s, &p);
+  if (st != BSA_OK) return st;
+  bsa_plan_cache::Entry e;
+  e.key = *req;
+  e.key.mask = nullptr;
+  e.dev = dev;
+  e.bytes = bytes;
+  e.plan = p;
+  e.last_use = ++c->tick;
+  hipError_t he = pool_alloc(dev, (size_t)bytes, &e.mask_copy);
+  if (he == hipSuccess) he = pool_alloc(dev, sizeof(unsigned long long), &e.guard);
+  if (he == hipSuccess) he = hipMemcpyAsync(e.mask_copy.ptr, req->mask, (size_t)bytes, hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess) he = event_get(dev, false, &e.copied);
+  if (he == hipSuccess) he = hipEventRecord(e.copied, s);
+  if (he != hipSuccess) {
+    drop_entry(e);
+    return fail(BSA_ERR_HIP, "caching the mask: %s", hipGetErrorString(he));
+  }
+  c->entries.push_back(e);
+  auto total = [&]() {
+    int64_t t = 0;
+    for (auto& x : c->entries) t += x.bytes;
+    return t;
+  };
+  while ((int)c->entries.size() > c->capacity ||
+         (c->max_bytes > 0 && total() > c->max_bytes && c->entries.size() > 1)) {
+    int lru = -1;
+    for (int i = 0; i < (int)c->entries.size(); ++i)
+      if (c->entries[i].plan != p && (lru < 0 || c->entries[i].last_use < c->entries[lru].last_use)) lru = i;
+    if (lru < 0) break;
+    drop_entry(c->entries[lru]);
+    c->entries.erase(c->entries.begin() + lru);
+  }
+  *out = p;
+  if (io) return run_impl(p, io->q, io->k, io->v, io->o, s, false, nullptr, nullptr, nullptr);
+  return BSA_OK;
+}
 
 }  // namespace
 
@@ -628,8 +750,11 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   return BSA_OK;
 }
 
+// guard: nullptr, or a device word that the kernels read as the task count
+// (0: the run does nothing; the speculative run of the plan cache).
 static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, const void* v, void* o,
-                           hipStream_t s, bool timed, float* attn_ms, float* merge_ms) {
+                           hipStream_t s, bool timed, float* attn_ms, float* merge_ms,
+                           const unsigned long long* guard) {
   if (!p) return fail(BSA_ERR_INVALID_ARG, "plan is NULL");
   if (!q || !k || !v || !o) return fail(BSA_ERR_INVALID_ARG, "NULL tensor pointer");
   for (const void* ptr : {q, k, v, (const void*)o})
@@ -649,7 +774,7 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   a.v = (const __bf16*)v;
   a.o = (__bf16*)o;
   a.tasks = (const Task*)p->tasks.ptr;
-  a.n_tasks = &((const MaskStats*)p->stats_dev.ptr)->n_tasks;
+  a.n_tasks = guard ? guard : &((const MaskStats*)p->stats_dev.ptr)->n_tasks;
   a.tcol = p->tcol;
   a.tbits = p->tbits;
   float* ws = (float*)p->ws.ptr;
@@ -683,6 +808,7 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   if (p->shape.split > 0) {
     MergeArgs m{};
     m.o = (__bf16*)o;
+    m.guard = guard;
     m.heads = a.heads;
     m.batch_stride = a.batch_stride;
     m.head_stride = a.head_stride;
@@ -716,12 +842,12 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
 }
 
 bsa_status bsa_run(const bsa_plan* p, const void* q, const void* k, const void* v, void* o, void* stream) {
-  return run_impl(p, q, k, v, o, (hipStream_t)stream, false, nullptr, nullptr);
+  return run_impl(p, q, k, v, o, (hipStream_t)stream, false, nullptr, nullptr, nullptr);
 }
 
 bsa_status bsa_run_timed(const bsa_plan* p, const void* q, const void* k, const void* v, void* o, void* stream,
                          float* attn_ms, float* merge_ms) {
-  return run_impl(p, q, k, v, o, (hipStream_t)stream, true, attn_ms, merge_ms);
+  return run_impl(p, q, k, v, o, (hipStream_t)stream, true, attn_ms, merge_ms, nullptr);
 }
 
 bsa_status bsa_plan_destroy(bsa_plan* p) {
@@ -836,90 +962,14 @@ bsa_status bsa_plan_cache_create(int32_t capacity, int64_t max_mask_bytes, bsa_p
 
 bsa_status bsa_plan_cache_get(bsa_plan_cache* c, const bsa_request* req, void* stream, bsa_plan** out,
                               int32_t* hit) {
-  if (!c || !out || !hit) return fail(BSA_ERR_INVALID_ARG, "NULL argument");
-  const bsa_status vs = validate_request(req);
-  if (vs != BSA_OK) return vs;
-  hipStream_t s = (hipStream_t)stream;
-  std::lock_guard<std::mutex> lk(c->mu);
-  int dev = 0;
-  HIP_TRY(hipGetDevice(&dev));
-  const int64_t bytes = (int64_t)folded(*req).H * cdiv(req->N, req->block_q) * cdiv(req->N, req->block_kv);
-  *hit = 0;
-  *out = nullptr;
-  // candidates: same request on this device, most recently used first
-  std::vector<int> cand;
-  for (int i = 0; i < (int)c->entries.size(); ++i)
-    if (c->entries[i].dev == dev && same_request(c->entries[i].key, *req)) cand.push_back(i);
-  std::sort(cand.begin(), cand.end(),
-            [&](int a, int b) { return c->entries[a].last_use > c->entries[b].last_use; });
-  if ((int)cand.size() > kMaxCompare) cand.resize(kMaxCompare);
-  if (!cand.empty()) {
-    CompareResult* host = pinned_compare();
-    if (!host) return fail(BSA_ERR_NO_MEMORY, "pinned host allocation failed");
-    DevBuf& fl = c->flags[dev];
-    if (!fl.ptr) {
-      HIP_TRY(pool_alloc(dev, sizeof(int32_t) * kMaxCompare, &fl));
-      HIP_TRY(hipMemset(fl.ptr, 0, sizeof(int32_t) * kMaxCompare));
-    }
-    CompareArgs a{};
-    a.mask = req->mask;
-    a.ncand = (int32_t)cand.size();
-    for (int k = 0; k < a.ncand; ++k) {
-      a.cand[k] = (const uint8_t*)c->entries[cand[k]].mask_copy.ptr;
-      HIP_TRY(hipStreamWaitEvent(s, c->entries[cand[k]].copied, 0));  // copy made on another stream
-    }
-    a.bytes = bytes;
-    a.flags = (int32_t*)fl.ptr;
-    thread_local unsigned long long seq = 0;  // the host record is per thread
-    ++seq;
-    HIP_TRY(launch_mask_compare(a, host, seq, s));
-    const bsa_status ws = wait_host_seq(&host->seq, seq, s, "mask comparison results");
-    if (ws != BSA_OK) return ws;
-    for (int k = 0; k < a.ncand; ++k) {
-      if (!host->differs[k]) {
-        bsa_plan_cache::Entry& e = c->entries[cand[k]];
-        e.last_use = ++c->tick;
-        *out = e.plan;
-        *hit = 1;
-        return BSA_OK;
-      }
-    }
-  }
-  // miss: plan, keep a copy of the mask, evict the least recently used
+  return cache_acquire(c, req, (hipStream_t)stream, nullptr, out, hit);
+}
+
+bsa_status bsa_plan_cache_run(bsa_plan_cache* c, const bsa_request* req, const void* q, const void* k,
+                              const void* v, void* o, void* stream, int32_t* hit) {
+  const RunIO io{q, k, v, o};
   bsa_plan* p = nullptr;
-  const bsa_status st = bsa_plan_create(req, stream, &p);
-  if (st != BSA_OK) return st;
-  bsa_plan_cache::Entry e;
-  e.key = *req;
-  e.key.mask = nullptr;
-  e.dev = dev;
-  e.bytes = bytes;
-  e.plan = p;
-  e.last_use = ++c->tick;
-  hipError_t he = pool_alloc(dev, (size_t)bytes, &e.mask_copy);
-  if (he == hipSuccess) he = hipMemcpyAsync(e.mask_copy.ptr, req->mask, (size_t)bytes, hipMemcpyDeviceToDevice, s);
-  if (he == hipSuccess) he = event_get(dev, false, &e.copied);
-  if (he == hipSuccess) he = hipEventRecord(e.copied, s);
-  if (he != hipSuccess) {
-    drop_entry(e);
-    return fail(BSA_ERR_HIP, "caching the mask: %s", hipGetErrorString(he));
-  }
-  c->entries.push_back(e);
-  auto total = [&]() {
-    int64_t t = 0;
-    for (auto& x : c->entries) t += x.bytes;
-    return t;
-  };
-  while ((int)c->entries.size() > c->capacity || (c->max_bytes > 0 && total() > c->max_bytes && c->entries.size() > 1)) {
-    int lru = -1;
-    for (int i = 0; i < (int)c->entries.size(); ++i)
-      if (c->entries[i].plan != p && (lru < 0 || c->entries[i].last_use < c->entries[lru].last_use)) lru = i;
-    if (lru < 0) break;
-    drop_entry(c->entries[lru]);
-    c->entries.erase(c->entries.begin() + lru);
-  }
-  *out = p;
-  return BSA_OK;
+  return cache_acquire(c, req, (hipStream_t)stream, &io, &p, hit);
 }
 
 bsa_status bsa_plan_cache_destroy(bsa_plan_cache* c) {
@@ -948,5 +998,6 @@ void drop_entry(bsa_plan_cache::Entry& e) {
     e.copied = nullptr;
   }
   pool_release(&e.mask_copy);
+  pool_release(&e.guard);
 }
 }  // namespace

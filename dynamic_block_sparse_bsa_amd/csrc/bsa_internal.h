@@ -41,6 +41,11 @@ struct CompareArgs {
   int32_t ncand;
   int64_t bytes;
   int32_t* flags;                       // device [kMaxCompare], zero on entry and on exit
+  // Optional guard of a speculative run of candidate 0's plan: set to that
+  // plan's task count when candidate 0 matches, else to 0 (the guarded
+  // kernels then exit at once).
+  const unsigned long long* spec_ntasks;
+  unsigned long long* guard;
 };
 // Host record of the check, written by the GPU into coherent host memory.
 struct CompareResult {
@@ -88,6 +93,7 @@ struct AttnArgs {
 
 struct MergeArgs {
   __bf16* o;
+  const unsigned long long* guard;  // nullptr, or a word that is 0 when the run must do nothing
   int64_t batch_stride;     // layout of O, as in AttnArgs
   int64_t head_stride;
   int32_t heads;

@@ -21,6 +21,7 @@ constexpr int kCols = 16;       // output columns per workgroup
 
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   __shared__ float wgt[kMaxParts][kMaxTq];
+  if (a.guard && *a.guard == 0ull) return;
   const int g = blockIdx.x;
   const int parts = a.parts[g];
   if (parts <= 1) return;

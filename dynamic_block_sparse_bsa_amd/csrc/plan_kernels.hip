@@ -456,12 +456,17 @@ __global__ __launch_bounds__(256) void k_mask_compare(const CompareArgs a) {
 }
 
 // Copies the flags to the host record (then the sequence number, system-scope
-// release) and clears them for the next check.
+// release), sets the speculative-run guard, and clears the flags for the next
+// check.
 __global__ __launch_bounds__(64) void k_compare_publish(int32_t* flags, int32_t ncand, CompareResult* host,
-                                                        unsigned long long seq) {
+                                                        unsigned long long seq,
+                                                        const unsigned long long* spec_ntasks,
+                                                        unsigned long long* guard) {
   const int t = threadIdx.x;
   if (t < kMaxCompare) {
-    host->differs[t] = t < ncand ? flags[t] : 1;
+    const int32_t f = t < ncand ? flags[t] : 1;
+    host->differs[t] = f;
+    if (t == 0 && guard) *guard = f == 0 ? *spec_ntasks : 0ull;
     flags[t] = 0;
   }
   __syncthreads();
@@ -475,7 +480,8 @@ hipError_t launch_mask_compare(const CompareArgs& a, CompareResult* host, unsign
   if (a.ncand < 1 || a.ncand > kMaxCompare) return hipErrorInvalidValue;
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((a.bytes + 4095) / 4096, 512));
   hipLaunchKernelGGL(k_mask_compare, dim3((unsigned)blocks, (unsigned)a.ncand), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_compare_publish, dim3(1), dim3(64), 0, s, a.flags, a.ncand, host, seq);
+  hipLaunchKernelGGL(k_compare_publish, dim3(1), dim3(64), 0, s, a.flags, a.ncand, host, seq, a.spec_ntasks,
+                     a.guard);
   return hipGetLastError();
 }
 

@@ -224,6 +224,18 @@ bsa_status bsa_plan_cache_create(int32_t capacity, int64_t max_mask_bytes, bsa_p
 bsa_status bsa_plan_cache_get(bsa_plan_cache* cache, const bsa_request* req, void* stream, bsa_plan** out,
                               int32_t* hit);
 
+/* O = BSA(Q, K, V) for `req` through the cache: bsa_plan_cache_get followed
+ * by bsa_run of the returned plan, with tensors as for bsa_run.  On a
+ * repeat the most recently used candidate plan is queued right behind the
+ * mask comparison, its kernels guarded by the comparison's verdict (they do
+ * nothing when it differs), so the host's wait for the verdict overlaps the
+ * attention work; another matching candidate or a new plan then runs after
+ * it and writes O.  *hit as for bsa_plan_cache_get.  Stream-ordered; returns
+ * once O's kernels are queued.  Errors: those of bsa_plan_cache_get and
+ * bsa_run. */
+bsa_status bsa_plan_cache_run(bsa_plan_cache* cache, const bsa_request* req, const void* q, const void* k,
+                              const void* v, void* o, void* stream, int32_t* hit);
+
 /* Destroys every cached plan (after their latest stream work) and the cache. */
 bsa_status bsa_plan_cache_destroy(bsa_plan_cache* cache);
 

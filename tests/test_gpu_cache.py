@@ -90,3 +90,41 @@ def test_plan_cache_ragged_and_unaligned_mask():
         assert_close(_run(p3, qd, kd, vd), oatt.attention(q, k, v, M3, *block), "unaligned changed mask")
     finally:
         cache.destroy()
+
+
+@pytest.mark.parametrize("force_split", [-1, 1])
+def test_plan_cache_run_speculative(force_split):
+    """bsa_plan_cache_run: the most recently used candidate runs behind the
+    comparison, guarded by its verdict.  Every output must match the oracle
+    for the mask passed, whether that candidate matched (hit), another one
+    did (hit on an older entry) or none did (miss, new plan); force_split=1
+    makes every split-K path (and its merge) part of the guarded run."""
+    dev = torch.device("cuda")
+    H, N, d, block = 2, 1300, 128, (64, 64)
+    masks = []
+    for s in range(3):
+        M, q, k, v = gen.random_case(H, N, d, *block, p=0.25 + 0.1 * s, seed=400 + s, empty_rows={0: [1]})
+        masks.append(M)
+    q, k, v = gen.qkv(H, N, d, (41, 42, 43))
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    refs = [oatt.attention(q, k, v, M, *block) for M in masks]
+    cache = bsa.PlanCache(capacity=3)
+
+    def go(i, want_hit):
+        out = torch.full(qd.shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        o, hit = cache.run(torch.from_numpy(masks[i]).to(dev), block, H, N, d, qd, kd, vd, out,
+                           force_split=force_split)
+        torch.cuda.synchronize()
+        assert hit == want_hit, (i, hit)
+        assert_close(o, refs[i], f"mask {i} hit {hit}")
+
+    try:
+        go(0, False)  # miss: plan and run
+        go(0, True)   # repeat: the speculated candidate matches
+        go(1, False)  # differs from the speculated candidate: guarded run does nothing, new plan
+        go(2, False)
+        go(0, True)   # candidate 0 (mask 2) differs, an older one matches
+        go(0, True)
+        go(1, True)
+    finally:
+        cache.destroy()
