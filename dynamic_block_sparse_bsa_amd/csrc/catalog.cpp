@@ -124,14 +124,18 @@ const std::vector<CatalogEntry>& catalog() {
 }
 
 uint64_t catalog_hash_value() {
-  uint64_t h = 1469598103934665603ull;  // FNV-1a over the entry names
-  for (auto& e : catalog()) {
-    for (char ch : e.name) {
-      h ^= (unsigned char)ch;
-      h *= 1099511628211ull;
-    }
-    h ^= 0xff;
+  // FNV-1a over every entry's name and parameters, so a table compiled for
+  // another catalog (including one that only changed a parameter) is refused
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&](unsigned char ch) {
+    h ^= ch;
     h *= 1099511628211ull;
+  };
+  for (auto& e : catalog()) {
+    for (char ch : e.name) mix((unsigned char)ch);
+    mix(0xff);
+    for (int v : {e.tq, e.tkv, e.d, e.split, e.xcd_remap, e.order})
+      for (int b = 0; b < 4; ++b) mix((unsigned char)(v >> (8 * b)));
   }
   return h;
 }
