@@ -107,6 +107,8 @@ def main():
     ap.add_argument("--requests", type=int, default=50, help="stream length for --config 5")
     ap.add_argument("--force-plan", type=int, default=-1)
     ap.add_argument("--force-split", type=int, default=-1)
+    ap.add_argument("--layout", default="HND", choices=["HND", "NHD"],
+                    help="tensor layout of Q, K, V and O ([H][N][d] or [N][H][d])")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -138,7 +140,9 @@ def main():
     cfg = gen.config(args.config)
     H, N, d = cfg["H"], cfg["N"], cfg["d"]
     q, k, v = (t.to(dev) for t in (cfg["q"], cfg["k"], cfg["v"]))
-    out = torch.empty((H, N, d), dtype=torch.bfloat16, device=dev)
+    if args.layout == "NHD":
+        q, k, v = (t.permute(1, 0, 2).contiguous() for t in (q, k, v))
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     # requests: (mask on device, block, flops)
     reqs = []
     nreq = args.requests if args.config == 5 else 1
@@ -153,7 +157,8 @@ def main():
 
     def request(i, want_info=False):
         Md, block, _, _ = reqs[i % len(reqs)]
-        p = bsa.plan(Md, block, H, N, d, force_plan=args.force_plan, force_split=args.force_split)
+        p = bsa.plan(Md, block, H, N, d, force_plan=args.force_plan, force_split=args.force_split,
+                     layout=args.layout)
         # returns once the request's last kernel has completed (HIP event wait)
         _, a_ms, m_ms = bsa.run_timed(p, q, k, v, out)
         info = p.info if want_info else None
@@ -192,6 +197,8 @@ def main():
         wl = f"{workload}: {len(reqs)} requests, H={H} N={N} d={d}, B re-drawn per request"
     else:
         wl = f"{workload}: H={H} N={N} d={d} B=({block[0]},{block[1]})"
+    if args.layout != "HND":
+        wl += f", layout {args.layout}"
     planning = [r - a - m for r, a, m in zip(req_ms, attn_ms, merge_ms)]
     res = {
         "metric": METRIC,
@@ -219,7 +226,7 @@ def main():
         "regime": info["regime"],
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": load_traffic(workload)},
+                     "traffic": load_traffic(workload) if args.layout == "HND" else None},
     }
     if args.no_cpu or args.config == 5:
         res["cpu_baseline"] = None
