@@ -228,7 +228,8 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
     p.tasks_upper = p.nqt;
     p.slots_upper = 0;
   }
-  p.ws_bytes = p.slots_upper * (int64_t)e.tq * (e.d + 2) * 4;
+  // per slot and query row: fp32 m and l, then d bf16 partial outputs
+  p.ws_bytes = p.slots_upper * (int64_t)e.tq * (2 * 4 + e.d * 2);
   return p;
 }
 
@@ -781,7 +782,7 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   const int64_t slots = p->shape.slots_upper;
   a.ws_m = ws;
   a.ws_l = ws ? ws + slots * e.tq : nullptr;
-  a.ws_o = ws ? ws + 2 * slots * e.tq : nullptr;
+  a.ws_o = ws ? reinterpret_cast<uint32_t*>(ws + 2 * slots * e.tq) : nullptr;
   // layout: HND = [batch*H][N][d] (one run of heads), NHD = [batch][N][H][d]
   const bool nhd = r.layout == BSA_LAYOUT_NHD;
   a.heads = nhd ? p->heads : r.H;

@@ -570,13 +570,17 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       a.ws_m[sl * TQ + r] = m_run;
       a.ws_l[sl * TQ + r] = l_tot;
     }
-    float* wo = a.ws_o + sl * (size_t)D * TQ;
+    // the partial output normalized by its own l, as bf16 pairs (d, d+1) so
+    // each lane stores 4 bytes and a wave's 32 rows fill 128 contiguous bytes
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    uint32_t* wo = a.ws_o + sl * (size_t)(D / 2) * TQ;
 #pragma unroll
     for (int b = 0; b < S::DB; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int dd = b * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        wo[(size_t)dd * TQ + r] = acc[b][v];
+      for (int v = 0; v < 16; v += 2) {
+        const int dd = b * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);  // even
+        const bf16x2 pr = {(__bf16)(acc[b][v] * inv), (__bf16)(acc[b][v + 1] * inv)};
+        wo[(size_t)(dd >> 1) * TQ + r] = __builtin_bit_cast(uint32_t, pr);
       }
   }
 #endif

@@ -5,11 +5,13 @@
 // exp2(m_p - m*).  A row whose partitions are all empty (l = 0) outputs zeros.
 //
 // One workgroup per (split query tile, 16 output columns), so even a few
-// split tiles spread over many CUs.  The per-row weights w_p / sum_p w_p l_p
+// split tiles spread over many CUs.  The per-row weights w_p l_p / sum_q w_q l_q
 // are computed once per workgroup (one thread per row) into LDS; the threads
-// then stream the partial accumulators, four output columns per thread item,
-// reading [slot][d][T_Q] rows contiguously.  HBM-bound: each partial element
-// is read once and each output element written once.
+// then stream the partial outputs, four output columns per thread item,
+// reading [slot][d/2][T_Q] rows of bf16 pairs contiguously.  Each partial is
+// its partition's output normalized by its own exponential sum, so the
+// weights carry l_p.  HBM-bound: each partial element is
+// read once and each output element written once.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -49,15 +51,16 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
       const float l = a.ws_l[s];
       const float w = l > 0.0f ? __builtin_amdgcn_exp2f(a.ws_m[s] - mstar) : 0.0f;
       den += w * l;
-      if (p < kMaxParts) wgt[p][t] = w;
+      if (p < kMaxParts) wgt[p][t] = w * l;  // the partials are normalized by their own l
     }
     inv = den > 0.0f ? 1.0f / den : 0.0f;
     for (int p = 0; p < min(parts, kMaxParts); ++p) wgt[p][t] *= inv;
   }
   __syncthreads();
-  // (2) out[r][c..c+3] = sum_p wgt[p][r] * O_p[c..c+3][r], c in this
-  // workgroup's kCols columns; the partition loop is unrolled so several
-  // partitions' loads are in flight together
+  // (2) out[r][c..c+3] = sum_p wgt[p][r] * O_p[c..c+3][r] (O_p normalized,
+  // stored as bf16 pairs), c in this workgroup's kCols columns; the
+  // partition loop is unrolled so several partitions' loads are in flight
+  // together
   const int nitems = TQ * (kCols / 4);
   for (int item = t; item < nitems; item += 256) {
     const int r = item % TQ;
@@ -81,11 +84,15 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
           if (a.ws_l[s] > 0.0f) den += __builtin_amdgcn_exp2f(a.ws_m[s] - ms) * a.ws_l[s];
         }
         const size_t s = (size_t)(sb + p) * TQ + r;
-        w = (a.ws_l[s] > 0.0f && den > 0.0f) ? __builtin_amdgcn_exp2f(a.ws_m[s] - ms) / den : 0.0f;
+        const float l = a.ws_l[s];
+        w = (l > 0.0f && den > 0.0f) ? __builtin_amdgcn_exp2f(a.ws_m[s] - ms) * l / den : 0.0f;
       }
-      const float* o = a.ws_o + (size_t)(sb + p) * D * TQ + (size_t)c * TQ + r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += w * o[(size_t)i * TQ];
+      const uint32_t* o = a.ws_o + (size_t)(sb + p) * (D / 2) * TQ + (size_t)(c >> 1) * TQ + r;
+      const uint32_t x0 = o[0], x1 = o[TQ];  // columns (c, c+1) and (c+2, c+3)
+      acc[0] += w * __uint_as_float(x0 << 16);
+      acc[1] += w * __uint_as_float(x0 & 0xffff0000u);
+      acc[2] += w * __uint_as_float(x1 << 16);
+      acc[3] += w * __uint_as_float(x1 & 0xffff0000u);
     }
     __bf16 ov[4];
 #pragma unroll
