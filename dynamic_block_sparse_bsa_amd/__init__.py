@@ -21,6 +21,7 @@ _lib = None
 BSA_DTYPE_BF16 = 1
 BSA_LAYOUT_HND = 0
 BSA_LAYOUT_NHD = 1
+SPLIT_STREAM = -2  # force_split value of the stream organization (BSA_SPLIT_STREAM)
 _LAYOUTS = {"HND": BSA_LAYOUT_HND, "NHD": BSA_LAYOUT_NHD}
 
 

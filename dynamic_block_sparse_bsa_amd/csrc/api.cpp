@@ -176,14 +176,14 @@ int device_cus(int dev) {
   return n;
 }
 
-int wg_per_cu_cached(int tq, int tkv, int d) {
+int wg_per_cu_cached(int tq, int tkv, int d, bool stream = false) {
   static std::mutex mu;
   static std::map<int, int> cache;
-  const int key = (tq << 20) | (tkv << 8) | d;
+  const int key = (tq << 20) | (tkv << 8) | d | (stream ? 1 << 30 : 0);
   std::lock_guard<std::mutex> lk(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  int n = attn_wg_per_cu(tq, tkv, d);
+  int n = attn_wg_per_cu(tq, tkv, d, stream);
   if (n <= 0) n = 1;
   cache[key] = n;
   return n;
@@ -196,6 +196,7 @@ int wg_per_cu_cached(int tq, int tkv, int d) {
 struct PlanShape {
   DimMap mq, mk;
   int split = 0;           // entries per partition, 0 = never split
+  int groups = 0;          // > 0: stream organization over this many workgroups
   int64_t tasks_upper = 0;
   int64_t slots_upper = 0;
   int64_t ws_bytes = 0;
@@ -213,6 +214,15 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
   const int64_t W = (int64_t)p.mq.refine * (int64_t)st.nnz;
   const int64_t row_max = (int64_t)p.mq.coarsen * st.max_row_nnz;
   int split = 0;
+  if (r.force_split == BSA_SPLIT_STREAM) {
+    // one equal range of entries per resident workgroup slot
+    const int64_t slots = (int64_t)device_cus(dev) * wg_per_cu_cached(e.tq, e.tkv, e.d, true);
+    p.groups = (int)std::max<int64_t>(1, std::min<int64_t>(slots, kMaxStreamGroups));
+    p.tasks_upper = p.nqt + p.groups;
+    p.slots_upper = 2 * (int64_t)p.groups;
+    p.ws_bytes = p.slots_upper * (int64_t)e.tq * (2 * 4 + e.d * 2);
+    return p;
+  }
   if (r.force_split > 0) {
     split = r.force_split;
   } else if (r.force_split < 0 && e.split) {
@@ -274,7 +284,7 @@ struct bsa_plan {
   MaskStats stats{};
   bsa_plan_info info{};
   DevBuf stats_dev, row_cnt, row_ptr, row_part, cols, trow_cnt, trow_ptr_buf, tcol_buf, tbits_buf, parts,
-      slot_off, tasks, ws;
+      slot_off, tasks, ws, seg_ptr;
   const int32_t* trow_ptr = nullptr;
   const int32_t* tcol = nullptr;
   const uint32_t* tbits = nullptr;
@@ -284,7 +294,7 @@ struct bsa_plan {
 
   ~bsa_plan() {
     for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &row_part, &cols, &trow_cnt, &trow_ptr_buf, &tcol_buf,
-                      &tbits_buf, &parts, &slot_off, &tasks, &ws})
+                      &tbits_buf, &parts, &slot_off, &tasks, &ws, &seg_ptr})
       pool_release(b);
     for (auto& e : ev) event_put(dev, true, e);
     event_put(dev, false, done);
@@ -330,7 +340,8 @@ bsa_status validate_request(const bsa_request* rq) {
     return fail(BSA_ERR_UNSUPPORTED, "H*N too large");
   if (r->force_plan >= (int)catalog().size() || r->force_plan < -1)
     return fail(BSA_ERR_INVALID_ARG, "force_plan %d out of range", r->force_plan);
-  if (r->force_split < -1) return fail(BSA_ERR_INVALID_ARG, "force_split %d invalid", r->force_split);
+  if (r->force_split < -1 && r->force_split != BSA_SPLIT_STREAM)
+    return fail(BSA_ERR_INVALID_ARG, "force_split %d invalid", r->force_split);
   if (r->workspace_limit < 0) return fail(BSA_ERR_INVALID_ARG, "negative workspace limit");
   return BSA_OK;
 }
@@ -713,12 +724,19 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   const int64_t max_len = shape.split > 0 ? shape.split
                                           : std::min<int64_t>((int64_t)shape.mq.coarsen * p->stats.max_row_nnz,
                                                               1 << 30);
-  HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split,
-                       chosen->order, (int32_t)max_len, (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr,
-                       dst, s));
+  if (shape.groups > 0) {
+    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)(shape.groups + 1), &p->seg_ptr));
+    HIP_TRY(launch_tasks_stream(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.groups,
+                                (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr,
+                                (int32_t*)p->seg_ptr.ptr, dst, s));
+  } else {
+    HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split, chosen->order,
+                         (int32_t)max_len, (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr,
+                         (Task*)p->tasks.ptr, dst, s));
+  }
   if (shape.slots_upper > 0) HIP_TRY(pool_alloc(p->dev, (size_t)shape.ws_bytes, &p->ws));
-  const int64_t gran = chosen->xcd_remap > 0 ? 8 * (int64_t)chosen->xcd_remap : 1;
-  p->grid = cdiv(std::max<int64_t>(shape.tasks_upper, 1), gran) * gran;
+  const int64_t gran = chosen->xcd_remap > 0 && shape.groups == 0 ? 8 * (int64_t)chosen->xcd_remap : 1;
+  p->grid = shape.groups > 0 ? shape.groups : cdiv(std::max<int64_t>(shape.tasks_upper, 1), gran) * gran;
   if (p->grid >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many tasks");
   HIP_TRY(hipGetLastError());
 
@@ -795,7 +813,8 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   a.coarsen_kv = p->shape.mk.coarsen;
   a.coarsen_q = p->shape.mq.coarsen;
   a.bq = r.block_q;
-  a.xcd_remap = e.xcd_remap;
+  a.xcd_remap = p->shape.groups > 0 ? 0 : e.xcd_remap;
+  a.seg_ptr = p->shape.groups > 0 ? (const int32_t*)p->seg_ptr.ptr : nullptr;
   a.grid = (int32_t)p->grid;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)r.d));
   bsa_plan* mp = const_cast<bsa_plan*>(p);
@@ -806,7 +825,7 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   }
   HIP_TRY(fn(a, (int)p->grid, s));
   if (timed) HIP_TRY(hipEventRecord(mp->ev[1], s));
-  if (p->shape.split > 0) {
+  if (p->shape.split > 0 || p->shape.groups > 0) {
     MergeArgs m{};
     m.o = (__bf16*)o;
     m.guard = guard;

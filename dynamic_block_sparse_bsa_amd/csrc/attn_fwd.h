@@ -167,7 +167,7 @@ template <int TQ, int TKV, int D>
 constexpr int kpf_depth() { return use_w3<TQ, TKV, D>() ? 2 : 4; }
 
 template <int TQ, int TKV, int D>
-__device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
+__device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using S = AttnShape<TQ, TKV, D>;
   constexpr int STAGE = S::KBYTES + S::VBYTES;
@@ -176,20 +176,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   constexpr int NSTAGE = S::NSTAGE;
   __shared__ __attribute__((aligned(1024))) unsigned char smem_arr[NSTAGE * STAGE];
   unsigned char* const smem = smem_arr;  // lambdas capture this pointer, not the array
-
-  // ---- task -------------------------------------------------------------
-  int bid = blockIdx.x;
-  if (a.xcd_remap > 0) {
-    // Workgroups are dealt to the 8 XCDs round-robin by id.  Remap so that
-    // each XCD receives runs of xcd_remap consecutive tasks (neighbouring
-    // query tiles of a head, which share K/V tiles in that XCD's L2), while
-    // all XCDs still advance through the task list together.
-    const int C = a.xcd_remap;
-    const int s = bid >> 3;
-    bid = (s / C) * (8 * C) + (bid & 7) * C + (s % C);
-  }
-  if ((unsigned long long)bid >= *a.n_tasks) return;
-  const Task task = a.tasks[bid];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -586,24 +572,60 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
 #endif
 }
 
+// Task dispatch: one task per workgroup (the task list's order, optionally
+// remapped over the XCDs), or with the stream organization (a separate
+// instantiation, so the one-task kernels keep their register allocation) the
+// workgroup's own run of tasks [seg_ptr[k], seg_ptr[k+1]), one after another.
+template <int TQ, int TKV, int D, bool STREAM>
+__device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
+  if constexpr (STREAM) {
+    if (*a.n_tasks == 0ull) return;  // a guarded run that must do nothing
+    const int t0 = a.seg_ptr[blockIdx.x], t1 = a.seg_ptr[blockIdx.x + 1];
+    for (int t = t0; t < t1; ++t) {
+      if (t > t0) __syncthreads();  // every wave is done with the previous task's LDS
+      attn_task<TQ, TKV, D>(a, a.tasks[t]);
+    }
+  } else {
+    int bid = blockIdx.x;
+    if (a.xcd_remap > 0) {
+      // Workgroups are dealt to the 8 XCDs round-robin by id.  Remap so that
+      // each XCD receives runs of xcd_remap consecutive tasks (neighbouring
+      // query tiles of a head, which share K/V tiles in that XCD's L2), while
+      // all XCDs still advance through the task list together.
+      const int C = a.xcd_remap;
+      const int s = bid >> 3;
+      bid = (s / C) * (8 * C) + (bid & 7) * C + (s % C);
+    }
+    if ((unsigned long long)bid >= *a.n_tasks) return;
+    attn_task<TQ, TKV, D>(a, a.tasks[bid]);
+  }
+}
+
 // Entry points: the generic kernel, and the one for 32-key tiles at d = 128
 // with at most 128 queries, whose registers are capped at 168 so three waves
 // fit a SIMD (the lower-occupancy schedule measured slower).
-template <int TQ, int TKV, int D>
+template <int TQ, int TKV, int D, bool STREAM>
 __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
-  attn_fwd_body<TQ, TKV, D>(a);
+  attn_fwd_body<TQ, TKV, D, STREAM>(a);
 }
-template <int TQ, int TKV, int D>
+template <int TQ, int TKV, int D, bool STREAM>
 __global__ __launch_bounds__(TQ * 2) __attribute__((amdgpu_waves_per_eu(3)))
 __attribute__((amdgpu_num_vgpr(168))) void attn_fwd_kernel_w3(const AttnArgs a) {
-  attn_fwd_body<TQ, TKV, D>(a);
+  attn_fwd_body<TQ, TKV, D, STREAM>(a);
+}
+template <int TQ, int TKV, int D, bool STREAM>
+void launch_attn_as(const AttnArgs& a, int grid, hipStream_t s) {
+  if constexpr (use_w3<TQ, TKV, D>())
+    hipLaunchKernelGGL((attn_fwd_kernel_w3<TQ, TKV, D, STREAM>), dim3(grid), dim3(TQ * 2), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<TQ, TKV, D, STREAM>), dim3(grid), dim3(TQ * 2), 0, s, a);
 }
 template <int TQ, int TKV, int D>
 hipError_t launch_attn(const AttnArgs& a, int grid, hipStream_t s) {
-  if constexpr (use_w3<TQ, TKV, D>())
-    hipLaunchKernelGGL((attn_fwd_kernel_w3<TQ, TKV, D>), dim3(grid), dim3(TQ * 2), 0, s, a);
+  if (a.seg_ptr)
+    launch_attn_as<TQ, TKV, D, true>(a, grid, s);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<TQ, TKV, D>), dim3(grid), dim3(TQ * 2), 0, s, a);
+    launch_attn_as<TQ, TKV, D, false>(a, grid, s);
   return hipGetLastError();
 }
 

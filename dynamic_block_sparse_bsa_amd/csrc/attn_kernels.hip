@@ -24,20 +24,24 @@ AttnLauncher attn_launcher(int tq, int tkv, int d) {
   return nullptr;
 }
 
-template <int TQ, int TKV, int D>
-static int wg_per_cu() {
+template <int TQ, int TKV, int D, bool STREAM>
+static int wg_per_cu_as() {
   int n = 0;
   hipError_t e;
   if constexpr (use_w3<TQ, TKV, D>())
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel_w3<TQ, TKV, D>, TQ * 2, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel_w3<TQ, TKV, D, STREAM>, TQ * 2, 0);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel<TQ, TKV, D>, TQ * 2, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel<TQ, TKV, D, STREAM>, TQ * 2, 0);
   return e == hipSuccess ? n : 0;
 }
+template <int TQ, int TKV, int D>
+static int wg_per_cu(bool stream) {
+  return stream ? wg_per_cu_as<TQ, TKV, D, true>() : wg_per_cu_as<TQ, TKV, D, false>();
+}
 
-int attn_wg_per_cu(int tq, int tkv, int d) {
+int attn_wg_per_cu(int tq, int tkv, int d, bool stream) {
 #define BSA_CASE(TQ_, TKV_, D_) \
-  if (tq == TQ_ && tkv == TKV_ && d == D_) return wg_per_cu<TQ_, TKV_, D_>();
+  if (tq == TQ_ && tkv == TKV_ && d == D_) return wg_per_cu<TQ_, TKV_, D_>(stream);
   BSA_CASE(64, 32, 128)
   BSA_CASE(64, 64, 128)
   BSA_CASE(128, 32, 128)

@@ -88,6 +88,8 @@ struct AttnArgs {
   int32_t bq;             // B_Q (membership decode when coarsen_q > 1)
   int32_t coarsen_q;
   int32_t xcd_remap;      // > 0: runs of this many consecutive tasks per XCD
+  const int32_t* seg_ptr; // stream organization: workgroup k runs tasks
+                          // [seg_ptr[k], seg_ptr[k+1]); nullptr: one task each
   int32_t grid;           // workgroups launched (multiple of 8 * xcd_remap when remapped)
   float scale_log2;       // log2(e) / sqrt(d)
 };
@@ -121,6 +123,10 @@ hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int
 hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPartial* part,
                        int32_t npart, MaskStats* st, MaskStats* host_st, unsigned long long seq,
                        hipStream_t s);
+constexpr int kMaxStreamGroups = 4096;  // workgroups of the stream organization
+hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
+                               int32_t refine_q, int32_t groups, int32_t* parts, int32_t* slot_base, Task* tasks,
+                               int32_t* seg_ptr, MaskStats* st, hipStream_t s);
 hipError_t launch_mask_compare(const CompareArgs& a, CompareResult* host, unsigned long long seq,
                                hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
@@ -138,6 +144,6 @@ hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s);
 // Attention kernel table: returns nullptr when (tq, tkv, d) has no kernel.
 AttnLauncher attn_launcher(int tq, int tkv, int d);
 // Resident workgroups per CU of that kernel (0 if it has none).
-int attn_wg_per_cu(int tq, int tkv, int d);
+int attn_wg_per_cu(int tq, int tkv, int d, bool stream);  // resident workgroups per CU
 
 }  // namespace bsa

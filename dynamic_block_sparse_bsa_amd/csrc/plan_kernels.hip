@@ -429,6 +429,130 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
   }
 }
 
+// Stream organization: the concatenated entries of all query tiles (head,
+// query tile, entry order; W in total) are cut into G equal ranges, one per
+// resident workgroup: workgroup k owns positions [ceil(kW/G), ceil((k+1)W/G)).
+// A query tile whose entries span several ranges becomes one task per range
+// (a partition with its own workspace slot); a tile without entries is one
+// empty task of the range its position falls in.  Tasks are written in
+// (tile, range) order, which is also range order, and seg_ptr[k] is the first
+// task of workgroup k (seg_ptr[G] = number of tasks).  G shrinks to W when W
+// < G, so every range owns at least one position.  One workgroup of 1024.
+__device__ inline int stream_group(long long x, long long W, int G) {
+  // the range that position x falls in (W > 0), clamped for trailing empty tiles
+  return (int)min((long long)G - 1, (x * G) / W);
+}
+
+__global__ __launch_bounds__(1024) void k_tasks_stream(const int32_t* __restrict__ trow_ptr, int32_t H,
+                                                       int32_t nqt_head, int32_t ntr, int32_t refine_q,
+                                                       int32_t G, int32_t* __restrict__ parts,
+                                                       int32_t* __restrict__ slot_base,
+                                                       Task* __restrict__ tasks,
+                                                       int32_t* __restrict__ seg_ptr, MaskStats* st) {
+  __shared__ int32_t lds[32];
+  __shared__ int32_t hist[kMaxStreamGroups];
+  const int t = threadIdx.x;
+  const int nqt = H * nqt_head;
+  // pass A: W = all entries
+  long long W = 0;
+  for (int base = 0; base < nqt; base += 4096) {
+    int32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int g = base + 4 * t + k;
+      if (g < nqt) {
+        const RowTasks r = row_tasks(trow_ptr, g, nqt_head, ntr, refine_q, 0);
+        sum += r.e - r.b;
+      }
+    }
+    int32_t tot;
+    (void)block_scan(sum, lds, &tot);
+    W += tot;
+  }
+  const int Ge = W > 0 ? (int)min((long long)G, W) : 1;
+  for (int k = t; k < G; k += 1024) hist[k] = 0;
+  __syncthreads();
+  // pass B: tasks in (tile, range) order, partition counts and slots
+  long long carry_p = 0;
+  int32_t carry_t = 0, carry_s = 0;
+  for (int base = 0; base < nqt; base += 4096) {
+    const int g0 = base + 4 * t;
+    RowTasks r[4];
+    int wfirst[4];
+    int32_t sum_n = 0, sum_t = 0, sum_s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r[k].p = 0;
+      r[k].b = r[k].e = 0;
+      if (g0 + k < nqt) {
+        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, 0);
+        sum_n += r[k].e - r[k].b;
+      }
+    }
+    int32_t tot_n, tot_t, tot_s;
+    long long pos = carry_p + block_scan(sum_n, lds, &tot_n);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (g0 + k >= nqt) break;
+      const int n = r[k].e - r[k].b;
+      wfirst[k] = W > 0 ? stream_group(pos, W, Ge) : 0;
+      const int wlast = n > 0 ? stream_group(pos + n - 1, W, Ge) : wfirst[k];
+      r[k].p = wlast - wfirst[k] + 1;
+      r[k].chunk = (int)(pos - carry_p);  // position within the chunk (restored below)
+      pos += n;
+      sum_t += r[k].p;
+      sum_s += r[k].p > 1 ? r[k].p : 0;
+    }
+    int32_t off_t = carry_t + block_scan(sum_t, lds, &tot_t);
+    int32_t off_s = carry_s + block_scan(sum_s, lds, &tot_s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int g = g0 + k;
+      if (g >= nqt) break;
+      const long long P = carry_p + r[k].chunk;
+      const int n = r[k].e - r[k].b;
+      parts[g] = r[k].p;
+      slot_base[g] = off_s;
+      for (int j = 0; j < r[k].p; ++j) {
+        const int w = wfirst[k] + j;
+        Task tk;
+        tk.head = r[k].h;
+        tk.qtile = r[k].qt;
+        if (n > 0) {
+          const long long cb = (w * W + Ge - 1) / Ge, ce = ((w + 1) * W + Ge - 1) / Ge;
+          tk.begin = r[k].b + (int)(max(P, cb) - P);
+          tk.end = r[k].b + (int)(min(P + n, ce) - P);
+        } else {
+          tk.begin = tk.end = r[k].b;
+        }
+        tk.slot = r[k].p > 1 ? off_s + j : -1;
+        tk.pad0 = w;
+        tk.pad1 = tk.pad2 = 0;
+        tasks[off_t + j] = tk;
+        atomicAdd(&hist[w], 1);
+      }
+      off_t += r[k].p;
+      off_s += r[k].p > 1 ? r[k].p : 0;
+    }
+    carry_p += tot_n;
+    carry_t += tot_t;
+    carry_s += tot_s;
+  }
+  if (t == 0) st->n_tasks = (unsigned long long)carry_t;
+  __syncthreads();
+  // seg_ptr = exclusive scan of the per-range task counts
+  int32_t carry = 0;
+  for (int base = 0; base < G; base += 1024) {
+    const int k = base + t;
+    const int32_t c = k < G ? hist[k] : 0;
+    int32_t tot;
+    const int32_t off = carry + block_scan(c, lds, &tot);
+    if (k < G) seg_ptr[k] = off;
+    carry += tot;
+  }
+  if (t == 0) seg_ptr[G] = carry;
+}
+
 // Plan cache, exact-repeat check: flags[c] = 1 when the request mask differs
 // from cached copy c anywhere (grid-stride over 16-byte words when both
 // pointers allow, else bytes; blockIdx.y = candidate).  Every writer stores
@@ -516,6 +640,15 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
   const size_t lds = (size_t)ntc * sizeof(uint32_t);
   hipLaunchKernelGGL(k_coarsen, dim3(H * ntr), dim3(256), lds, s, row_ptr, cols, nqb, cq, ckv, ntr,
                      ntc, trow_cnt, trow_ptr, tcol, tbits);
+  return hipGetLastError();
+}
+
+hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
+                               int32_t refine_q, int32_t groups, int32_t* parts, int32_t* slot_base, Task* tasks,
+                               int32_t* seg_ptr, MaskStats* st, hipStream_t s) {
+  if (groups < 1 || groups > kMaxStreamGroups) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tasks_stream, dim3(1), dim3(1024), 0, s, trow_ptr, H, nqt_head, ntr, refine_q, groups,
+                     parts, slot_base, tasks, seg_ptr, st);
   return hipGetLastError();
 }
 

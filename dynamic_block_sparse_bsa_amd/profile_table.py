@@ -30,6 +30,7 @@ import argparse
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -146,7 +147,9 @@ def reference_rows(q, k, v, M, block, rows):
     return out
 
 
-def profile(cases, reps=5, warmup=3, log=print):
+def profile(cases, reps=5, warmup=3, log=print, plans=None):
+    """plans: optional regular expression; only catalog entries whose names
+    match it are profiled (to add new entries to existing records)."""
     import numpy as np
     import torch
 
@@ -168,6 +171,8 @@ def profile(cases, reps=5, warmup=3, log=print):
         lat = {}
         stats = None
         for e in cat:
+            if plans and not re.search(plans, e["name"]):
+                continue
             if not bsa.eligible(e["id"], H, N, d, (BQ, BKV)):
                 continue
             try:
@@ -427,6 +432,7 @@ def main():
     ap.add_argument("--corpus", default="base", choices=["base", "extra", "all"],
                     help="which synthetic corpus to profile")
     ap.add_argument("--shard", default=None, help="i/n: profile every n-th case starting at i")
+    ap.add_argument("--plans", default=None, help="profile only catalog entries matching this regex")
     ap.add_argument("--partition", default="auto",
                     help="intervals | tree:<depth> | auto (cross-validated choice)")
     a = ap.parse_args()
@@ -448,7 +454,7 @@ def main():
         if a.shard:
             i, n = (int(x) for x in a.shard.split("/"))
             cases = cases[i::n]
-        recs = profile(cases, log=lambda s: print(s, flush=True))
+        recs = profile(cases, log=lambda s: print(s, flush=True), plans=a.plans)
         if a.records:
             with open(a.records, "w") as f:
                 json.dump(recs, f)

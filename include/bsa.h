@@ -54,6 +54,7 @@ enum { BSA_DTYPE_BF16 = 1 };
  *   BSA_LAYOUT_NHD  [batch][N][H][d]  (a token's heads adjacent; rows of one
  *                                      head are H*d elements apart) */
 enum { BSA_LAYOUT_HND = 0, BSA_LAYOUT_NHD = 1 };
+enum { BSA_SPLIT_STREAM = -2 };
 
 /* Opaque prepared plan: owns the block-CSR, the selected plan's metadata
  * (tile lists, membership bits, tasks) and its split-K workspace. */
@@ -75,7 +76,9 @@ typedef struct {
   int32_t force_plan;  /* -1: regime table selection; >= 0: that catalog entry
                           (must be eligible, else BSA_ERR_UNSUPPORTED)          */
   int32_t force_split; /* -1: the plan's own split rule; 0: never split;
-                          k > 0: at most k K/V items per task                   */
+                          k > 0: at most k K/V items per task;
+                          BSA_SPLIT_STREAM: equal ranges of the concatenated
+                          tile-list entries, one per resident workgroup       */
   int32_t batch;       /* batch entries, 0 or 1 = one                          */
   int64_t workspace_limit; /* bytes of split-K workspace allowed; 0 = no limit */
   /* device, uint8 [batch][H][ceil(N/B_Q)][ceil(N/B_KV)], nonzero = active

@@ -92,7 +92,7 @@ def test_plan_cache_ragged_and_unaligned_mask():
         cache.destroy()
 
 
-@pytest.mark.parametrize("force_split", [-1, 1])
+@pytest.mark.parametrize("force_split", [-1, 1, -2])
 def test_plan_cache_run_speculative(force_split):
     """bsa_plan_cache_run: the most recently used candidate runs behind the
     comparison, guarded by its verdict.  Every output must match the oracle

@@ -55,7 +55,7 @@ def test_layout_and_batch_all_plans(layout, batch, H, N, block):
     plans = [e["id"] for e in bsa.catalog() if bsa.eligible(e["id"], H, N, d, block, batch=batch, layout=layout)]
     assert len(plans) >= 6
     for pid in plans:
-        for fs in (-1, 1):
+        for fs in (-1, 1, bsa.SPLIT_STREAM):
             p = bsa.plan(Md, block, H, N, d, force_plan=pid, force_split=fs, batch=batch, layout=layout)
             out = torch.full(qd.shape, float("nan"), dtype=torch.bfloat16, device=dev)
             bsa.run(p, qd, kd, vd, out)

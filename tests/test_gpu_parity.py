@@ -34,7 +34,7 @@ def test_c1_every_eligible_plan(c1):
     plans = _eligible_plans(1, 1024, 64, (64, 64))
     assert len(plans) >= 6
     for pid in plans:
-        for fs in (-1, 0, 2):
+        for fs in (-1, 0, 2, bsa.SPLIT_STREAM):
             p, out = gpu_run(cfg["mask"], cfg["q"], cfg["k"], cfg["v"], (64, 64), force_plan=pid,
                              force_split=fs)
             assert_close(out, ref, f"plan {pid} split {fs}")
@@ -57,7 +57,7 @@ def test_small_all_plans(block, N):
     plans = _eligible_plans(H, N, d, block)
     assert plans
     for pid in plans:
-        for fs in (-1, 1):
+        for fs in (-1, 1, bsa.SPLIT_STREAM):
             p, out = gpu_run(M, q, k, v, block, force_plan=pid, force_split=fs)
             assert_close(out, ref, f"B={block} N={N} plan {pid} split {fs}")
             cov, cq, ckv = tile_cells(p, block, N)

@@ -47,6 +47,31 @@ def _expected_tasks(rp, H, nqb, nqt_head, refine_q, split):
     return out
 
 
+def _expected_stream(rp, H, nqb, nqt_head, refine_q, G):
+    """Stream organization: the concatenated entries (W) cut into
+    Ge = min(G, W) ranges [ceil(kW/Ge), ceil((k+1)W/Ge)); a tile becomes one
+    task per range it overlaps (an empty tile: one task at its position)."""
+    rows = []
+    for h in range(H):
+        for qt in range(nqt_head):
+            i = h * nqb + qt // refine_q
+            rows.append((h, qt, int(rp[i]), int(rp[i + 1])))
+    W = sum(e - b for _, _, b, e in rows)
+    Ge = min(G, W) if W > 0 else 1
+    out, P = [], 0
+    for h, qt, b, e in rows:
+        n = e - b
+        if n == 0:
+            out.append((h, qt, b, b, False))
+            continue
+        w0, w1 = min(Ge - 1, P * Ge // W), min(Ge - 1, (P + n - 1) * Ge // W)
+        for w in range(w0, w1 + 1):
+            cb, ce = -(-w * W // Ge), -(-(w + 1) * W // Ge)
+            out.append((h, qt, b + max(P, cb) - P, b + min(P + n, ce) - P, w1 > w0))
+        P += n
+    return out, W, Ge
+
+
 CASES = [((64, 64), 40000, 8), ((128, 128), 9000, 6)]
 
 
@@ -105,3 +130,49 @@ def test_task_organizations(block, N, H):
         p.destroy()
         checked += 1
     assert checked >= 6
+
+
+@pytest.mark.parametrize("block,N,H", CASES + [((64, 64), 3000, 1)])
+def test_stream_organization(block, N, H):
+    """force_split = SPLIT_STREAM: tasks are the tiles' intersections with G
+    equal entry ranges (G = the plan's grid), in tile order; every range holds
+    floor or ceil of W/G entries; sampled rows match the oracle."""
+    d = 128
+    M = gen.mask_clustered(H, N, *block, seed=777 + N, rho=(0.05, 0.45), p_empty_head=0.25)
+    nqb = M.shape[1]
+    dev = torch.device("cuda")
+    Md = torch.from_numpy(np.ascontiguousarray(M)).to(dev)
+    q, k, v = gen.qkv(H, N, d, (21, 22, 23))
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    rng = np.random.default_rng(N + 1)
+    rows = {h: np.unique(np.concatenate([rng.integers(0, N, 64), [0, N - 1]])) for h in range(H)}
+    ref = oatt.attention_rows(q, k, v, M, block[0], block[1], rows)
+    checked = 0
+    for e in bsa.catalog():
+        if e["order"] != 0 or e["xcd_remap"] != 0 or e["split"] != 1 or not bsa.eligible(e["id"], H, N, d, block):
+            continue
+        p = bsa.plan(Md, block, H, N, d, force_plan=e["id"], force_split=bsa.SPLIT_STREAM)
+        info = p.info
+        label = f"{e['name']} B={block} N={N} H={H}"
+        out = torch.full((H, N, d), float("nan"), dtype=torch.bfloat16, device=dev)
+        bsa.run(p, qd, kd, vd, out)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any().item(), f"{label}: unwritten rows"
+        err = np.concatenate([np.abs(out[h, torch.from_numpy(r).to(dev)].float().cpu().numpy()
+                                     .astype(np.float64) - ref[h]) for h, r in rows.items()])
+        assert err.max() <= MAX_ERR and err.mean() <= MEAN_ERR, f"{label}: max {err.max():.3e} mean {err.mean():.3e}"
+        if info["coarsen_q"] == 1 and info["coarsen_kv"] == 1:
+            rp, _ = p.export_csr()
+            head, qt, beg, end, slot = p.export_tasks()
+            nqt_head = -(-N // info["tile_q"])
+            exp, W, Ge = _expected_stream(rp, H, nqb, nqt_head, info["refine_q"], info["grid"])
+            got = list(zip(head.tolist(), qt.tolist(), beg.tolist(), end.tolist(), (slot >= 0).tolist()))
+            assert got == exp, f"{label}: stream tasks"
+            s = slot[slot >= 0]
+            assert len(np.unique(s)) == len(s), f"{label}: shared slot"
+            # range sizes: each range is floor or ceil of W / Ge entries
+            sizes = [-(-(w + 1) * W // Ge) - -(-w * W // Ge) for w in range(Ge)]
+            assert min(sizes) >= W // Ge and max(sizes) <= -(-W // Ge)
+        p.destroy()
+        checked += 1
+    assert checked >= 3
