@@ -623,22 +623,32 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   HIP_TRY(pool_alloc(p->dev, sizeof(MaskStats), &p->stats_dev));
   HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nrows + 1), &p->row_ptr));
   MaskStats* dst = (MaskStats*)p->stats_dev.ptr;
-  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
-  const int npart = row_count_blocks(nrows);
-  HIP_TRY(pool_alloc(p->dev, sizeof(RowPartial) * (size_t)npart, &p->row_part));
-  RowPartial* part = (RowPartial*)p->row_part.ptr;
-  HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, part, s));
   thread_local unsigned long long seq = 0;  // the host statistics buffer is per thread
   ++seq;
-  HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, host, seq, s));
-  // When a column array sized for every block is modest, the compaction is
-  // queued before the statistics synchronization, so it overlaps the host's
-  // wait and plan selection.
   const size_t cols_bound = sizeof(int32_t) * (size_t)nrows * (size_t)p->nkb;
-  const bool early_compact = cols_bound <= kEarlyCompactBytes;
-  if (early_compact) {
+  bool early_compact;
+  if (mask_small_ok(r.mask, nrows, p->nkb)) {
+    // small mask: counts, statistics, scan and compaction in one launch
+    early_compact = true;
     HIP_TRY(pool_alloc(p->dev, cols_bound, &p->cols));
-    HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
+    HIP_TRY(launch_mask_small(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, dst, host,
+                              seq, s));
+  } else {
+    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
+    const int npart = row_count_blocks(nrows);
+    HIP_TRY(pool_alloc(p->dev, sizeof(RowPartial) * (size_t)npart, &p->row_part));
+    RowPartial* part = (RowPartial*)p->row_part.ptr;
+    HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, part, s));
+    HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, host, seq,
+                        s));
+    // When a column array sized for every block is modest, the compaction is
+    // queued before the statistics synchronization, so it overlaps the host's
+    // wait and plan selection.
+    early_compact = cols_bound <= kEarlyCompactBytes;
+    if (early_compact) {
+      HIP_TRY(pool_alloc(p->dev, cols_bound, &p->cols));
+      HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
+    }
   }
   // Wait for the statistics alone (the compaction may still run): spin on the
   // sequence number the scan kernel stores last.

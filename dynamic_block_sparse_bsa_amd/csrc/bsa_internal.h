@@ -129,6 +129,16 @@ hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_h
                                int32_t* seg_ptr, MaskStats* st, hipStream_t s);
 hipError_t launch_mask_compare(const CompareArgs& a, CompareResult* host, unsigned long long seq,
                                hipStream_t s);
+// Single-launch mask state (counts, statistics, scan, compaction) for masks
+// of at most kSmallMaskBytes bytes, kSmallMaskRows rows and kSmallMaskCols
+// columns at a 16-byte aligned address; outputs as launch_row_count +
+// launch_scan + launch_compact.
+constexpr int kSmallMaskBytes = 32768;
+constexpr int kSmallMaskRows = 2048;
+constexpr int kSmallMaskCols = 256;
+bool mask_small_ok(const uint8_t* mask, int32_t nrows, int32_t nkb);
+hipError_t launch_mask_small(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_ptr, int32_t* cols,
+                             MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
                           int32_t* cols, hipStream_t s);
 hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,

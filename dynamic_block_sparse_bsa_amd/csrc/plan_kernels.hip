@@ -25,6 +25,32 @@ __device__ inline unsigned prefix_count(unsigned long long ballot) {
                                    __builtin_amdgcn_mbcnt_lo((unsigned)ballot, 0u));
 }
 
+// Hand-over of a record to the host through fine-grained host memory: the
+// fields are written with system-scope (write-through) stores, the wave waits
+// until they have completed (s_waitcnt vmcnt(0)), and only then stores the
+// sequence number that the host spins on.  A system-scope release would in
+// addition write back every dirty line of the XCD's L2 (buffer_wbl2), which
+// costs microseconds after a kernel that wrote megabytes and which the host,
+// reading only this record, does not need.
+template <class T>
+__device__ inline void sys_store(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ inline void sys_publish_seq(unsigned long long* p, unsigned long long seq) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the field stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  sys_store(p, seq);
+}
+__device__ inline void publish_stats(MaskStats* h, const MaskStats& r) {
+  sys_store(&h->nnz, r.nnz);
+  sys_store(&h->long_run, r.long_run);
+  sys_store(&h->max_row_nnz, r.max_row_nnz);
+  sys_store(&h->empty_rows, r.empty_rows);
+  sys_store(&h->n_tasks, 0ull);
+  sys_publish_seq(&h->seq, r.seq);
+}
+
 // Active count per query-block row, and per-workgroup partial statistics:
 // active blocks lying in runs of length >= 2 (an active block whose left or
 // right neighbour in the row is active; paper section 5.1), the largest row
@@ -173,16 +199,8 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
       r.n_tasks = 0;
       r.seq = seq;
       *st = r;
-      if (host_st) {
-        // fine-grained host memory, read by the host while this stream runs
-        // on: the fields, then (system-scope release) the sequence number
-        host_st->nnz = r.nnz;
-        host_st->long_run = r.long_run;
-        host_st->max_row_nnz = r.max_row_nnz;
-        host_st->empty_rows = r.empty_rows;
-        host_st->n_tasks = 0;
-        __hip_atomic_store(&host_st->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-      }
+      // fine-grained host memory, read by the host while this stream runs on
+      if (host_st) publish_stats(host_st, r);
     }
   }
 }
@@ -202,6 +220,139 @@ __global__ __launch_bounds__(256) void k_compact(const uint8_t* __restrict__ mas
     const unsigned long long ba = __ballot(a);
     if (a) cols[out + (int)prefix_count(ba)] = p;
     out += __popcll(ba);
+  }
+}
+
+// Bit i (i < 4) set iff byte i of x is nonzero: per byte, adding 0x7f to
+// its low seven bits sets bit 7 iff they are nonzero (no carry leaves the
+// byte), OR-ing x adds its own bit 7; the four byte flags are then gathered.
+__device__ inline uint32_t nz_bits4(uint32_t x) {
+  const uint32_t y = (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
+  return ((y >> 7) | (y >> 14) | (y >> 21) | (y >> 28)) & 0xfu;
+}
+
+// The whole mask state of a small mask in one launch (one workgroup of 1024):
+// the mask is packed into a bitmap in LDS (one 32-bit word of 32 consecutive
+// mask bytes per thread, from two 16-byte loads), then one thread per
+// query-block row counts its active blocks and those with an active left or
+// right neighbour, the counts are scanned into row_ptr, the statistics are
+// stored (and published to the host, sequence number last), and only then
+// are the columns compacted from the bitmap, so the host's plan selection
+// overlaps the compaction.  Same outputs as k_row_count + k_scan + k_compact.
+__global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__ mask, int32_t nrows,
+                                                     int32_t nkb, int32_t* __restrict__ row_ptr,
+                                                     int32_t* __restrict__ cols, MaskStats* st,
+                                                     MaskStats* host_st, unsigned long long seq) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ uint32_t bits[kSmallMaskBytes / 32 + 1];  // + a zero word read past the last row
+  __shared__ int32_t off[kSmallMaskRows];
+  __shared__ int32_t lds[32];
+  __shared__ unsigned long long s_long[16];
+  __shared__ unsigned s_max[16], s_empty[16];
+  const int t = threadIdx.x;
+  const int bytes = nrows * nkb;
+  const int nwords = (bytes + 31) >> 5;
+  // pack (the host only picks this kernel for a 16-byte aligned mask)
+  for (int i = t; i < nwords; i += 1024) {
+    const int b0 = i << 5;
+    uint32_t w = 0;
+    if (b0 + 32 <= bytes) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(mask + b0)[0];
+      const u32x4 y = reinterpret_cast<const u32x4*>(mask + b0)[1];
+      w = nz_bits4(x[0]) | (nz_bits4(x[1]) << 4) | (nz_bits4(x[2]) << 8) | (nz_bits4(x[3]) << 12) |
+          (nz_bits4(y[0]) << 16) | (nz_bits4(y[1]) << 20) | (nz_bits4(y[2]) << 24) | (nz_bits4(y[3]) << 28);
+    } else {
+      for (int j = 0; b0 + j < bytes; ++j) w |= (uint32_t)(mask[b0 + j] != 0) << j;
+    }
+    bits[i] = w;
+  }
+  if (t == 0) bits[nwords] = 0u;
+  __syncthreads();
+  // columns [32k, 32k + 32) of row r, zero past nkb
+  auto row_word = [&](int r, int k) -> uint32_t {
+    const int c0 = k << 5;
+    const int b = r * nkb + c0;
+    const int wi = b >> 5, sh = b & 31;
+    uint32_t v = bits[wi] >> sh;
+    if (sh) v |= bits[wi + 1] << (32 - sh);
+    const int rem = nkb - c0;
+    if (rem < 32) v &= (1u << rem) - 1u;
+    return v;
+  };
+  const int nw = (nkb + 31) >> 5;
+  // per-row counts and run statistics, one thread per row
+  unsigned long long lng_t = 0;
+  unsigned max_t = 0, empty_t = 0;
+  for (int r = t; r < nrows; r += 1024) {
+    unsigned cnt = 0, lng = 0;
+    uint32_t prev = 0u, cur = row_word(r, 0);
+    for (int k = 0; k < nw; ++k) {
+      const uint32_t next = k + 1 < nw ? row_word(r, k + 1) : 0u;
+      const uint32_t left = (cur << 1) | (prev >> 31);
+      const uint32_t right = (cur >> 1) | (next << 31);
+      cnt += __popc(cur);
+      lng += __popc(cur & (left | right));
+      prev = cur;
+      cur = next;
+    }
+    off[r] = (int32_t)cnt;
+    lng_t += lng;
+    max_t = max(max_t, cnt);
+    empty_t += (cnt == 0);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lng_t += __shfl_xor(lng_t, o, 64);
+    max_t = max(max_t, (unsigned)__shfl_xor((int)max_t, o, 64));
+    empty_t += (unsigned)__shfl_xor((int)empty_t, o, 64);
+  }
+  if ((t & 63) == 0) {
+    s_long[t >> 6] = lng_t;
+    s_max[t >> 6] = max_t;
+    s_empty[t >> 6] = empty_t;
+  }
+  __syncthreads();
+  // exclusive scan of the counts (in place in LDS, and to row_ptr)
+  int32_t carry = 0;
+  for (int base = 0; base < nrows; base += 1024) {
+    const int i = base + t;
+    const int32_t v = i < nrows ? off[i] : 0;
+    int32_t tot;
+    const int32_t ex = carry + block_scan(v, lds, &tot);
+    if (i < nrows) {
+      off[i] = ex;
+      row_ptr[i] = ex;
+    }
+    carry += tot;
+  }
+  if (t == 0) {
+    row_ptr[nrows] = carry;
+    MaskStats r;
+    r.nnz = (unsigned long long)carry;
+    r.long_run = 0;
+    r.max_row_nnz = 0;
+    r.empty_rows = 0;
+    for (int w = 0; w < 16; ++w) {
+      r.long_run += s_long[w];
+      r.max_row_nnz = max(r.max_row_nnz, s_max[w]);
+      r.empty_rows += s_empty[w];
+    }
+    r.n_tasks = 0;
+    r.seq = seq;
+    *st = r;
+    if (host_st) publish_stats(host_st, r);
+  }
+  // column compaction, one thread per row (each row's offset is its own
+  // thread's scan result, so no barrier is needed before it)
+  for (int r = t; r < nrows; r += 1024) {
+    int32_t o = off[r];
+    for (int k = 0; k < nw; ++k) {
+      uint32_t v = row_word(r, k);
+      while (v) {
+        cols[o++] = (k << 5) + __ffs(v) - 1;
+        v &= v - 1u;
+      }
+    }
   }
 }
 
@@ -589,12 +740,12 @@ __global__ __launch_bounds__(64) void k_compare_publish(int32_t* flags, int32_t 
   const int t = threadIdx.x;
   if (t < kMaxCompare) {
     const int32_t f = t < ncand ? flags[t] : 1;
-    host->differs[t] = f;
+    sys_store(&host->differs[t], f);
     if (t == 0 && guard) *guard = f == 0 ? *spec_ntasks : 0ull;
     flags[t] = 0;
   }
-  __syncthreads();
-  if (t == 0) __hip_atomic_store(&host->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  // one wave: its own field stores are the ones the wait covers
+  if (t == 0) sys_publish_seq(&host->seq, seq);
 }
 
 }  // namespace
@@ -622,6 +773,19 @@ hipError_t launch_scan(const int32_t* in, int32_t* out, int32_t n, const RowPart
                        int32_t npart, MaskStats* st, MaskStats* host_st, unsigned long long seq,
                        hipStream_t s) {
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, in, out, n, part, npart, st, host_st, seq);
+  return hipGetLastError();
+}
+
+bool mask_small_ok(const uint8_t* mask, int32_t nrows, int32_t nkb) {
+  return ((uintptr_t)mask & 15) == 0 && nrows <= kSmallMaskRows && nkb <= kSmallMaskCols &&
+         (int64_t)nrows * nkb <= kSmallMaskBytes;
+}
+
+hipError_t launch_mask_small(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_ptr, int32_t* cols,
+                             MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s) {
+  if (!mask_small_ok(mask, nrows, nkb)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mask_small, dim3(1), dim3(1024), 0, s, mask, nrows, nkb, row_ptr, cols, st, host_st,
+                     seq);
   return hipGetLastError();
 }
 
