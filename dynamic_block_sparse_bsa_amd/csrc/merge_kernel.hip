@@ -5,107 +5,154 @@
 // exp2(m_p - m*).  A row whose partitions are all empty (l = 0) outputs zeros.
 //
 // One workgroup per (split query tile, 16 output columns), so even a few
-// split tiles spread over many CUs.  The per-row weights w_p l_p / sum_q w_q l_q
-// are computed once per workgroup (one thread per row) into LDS; the threads
-// then stream the partial outputs, four output columns per thread item,
-// reading [slot][d/2][T_Q] rows of bf16 pairs contiguously.  Each partial is
-// its partition's output normalized by its own exponential sum, so the
-// weights carry l_p.  HBM-bound: each partial element is
-// read once and each output element written once.
+// split tiles spread over many CUs.  256 is a multiple of T_Q, so every thread
+// owns one row (t mod T_Q) and 4-column quads of it; it computes its row's
+// weights w_p l_p / sum_q w_q l_q in registers (each partial is its
+// partition's output normalized by its own exponential sum, so the weights
+// carry l_p) and streams the partial outputs, stored as [slot][d/2][T_Q] bf16
+// pairs, with the loads of all partitions in flight together (addresses past
+// the last partition are clamped to it and weighted 0).  No LDS and no
+// barrier.  HBM-bound: each partial element is read once and each output
+// element written once.
 #include "bsa_internal.h"
 
 namespace bsa {
 namespace {
 
-constexpr int kMaxParts = 32;   // partitions whose weights are held in LDS
 constexpr int kMaxTq = 256;
 constexpr int kCols = 16;       // output columns per workgroup
 
+struct MergeRow {
+  const MergeArgs* a;
+  int sb, parts, TQ, r;
+  size_t o_row;  // output element offset of the row
+};
+
+// Weights of row r for partitions [0, P) (P >= parts; entries past parts are 0).
+template <int P>
+__device__ __forceinline__ void row_weights(const MergeRow& m, float (&w)[P]) {
+  const MergeArgs& a = *m.a;
+  float mp[P], lp[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const size_t s = (size_t)(m.sb + min(p, m.parts - 1)) * m.TQ + m.r;
+    mp[p] = a.ws_m[s];
+    lp[p] = p < m.parts ? a.ws_l[s] : 0.0f;
+  }
+  float mstar = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (lp[p] > 0.0f) mstar = fmaxf(mstar, mp[p]);
+  float den = 0.0f;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    w[p] = lp[p] > 0.0f ? __builtin_amdgcn_exp2f(mp[p] - mstar) * lp[p] : 0.0f;
+    den += w[p];
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+  for (int p = 0; p < P; ++p) w[p] *= inv;
+}
+
+__device__ __forceinline__ void store_quad(const MergeRow& m, int c, const float (&acc)[4]) {
+  __bf16 ov[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc[i];
+  *reinterpret_cast<uint2*>(m.a->o + m.o_row + c) = *reinterpret_cast<const uint2*>(ov);
+}
+
+// Up to P partitions: weights and every partial load of a quad in registers.
+template <int P>
+__device__ __forceinline__ void merge_row(const MergeRow& m, int q0, int qstep) {
+  const MergeArgs& a = *m.a;
+  float w[P];
+  row_weights<P>(m, w);
+  for (int qi = q0; qi < kCols / 4; qi += qstep) {
+    const int c = blockIdx.y * kCols + qi * 4;
+    uint32_t x0[P], x1[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t* o = a.ws_o + (size_t)(m.sb + min(p, m.parts - 1)) * (a.d / 2) * m.TQ +
+                          (size_t)(c >> 1) * m.TQ + m.r;
+      x0[p] = o[0];      // columns (c, c+1)
+      x1[p] = o[m.TQ];   // columns (c+2, c+3)
+    }
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      acc[0] += w[p] * __uint_as_float(x0[p] << 16);
+      acc[1] += w[p] * __uint_as_float(x0[p] & 0xffff0000u);
+      acc[2] += w[p] * __uint_as_float(x1[p] << 16);
+      acc[3] += w[p] * __uint_as_float(x1[p] & 0xffff0000u);
+    }
+    store_quad(m, c, acc);
+  }
+}
+
+// Any number of partitions: the weights are recomputed per partition from
+// two passes over (m, l) (rare: more than 16 partitions).
+__device__ void merge_row_any(const MergeRow& m, int q0, int qstep) {
+  const MergeArgs& a = *m.a;
+  float mstar = -INFINITY, den = 0.0f;
+  for (int p = 0; p < m.parts; ++p) {
+    const size_t s = (size_t)(m.sb + p) * m.TQ + m.r;
+    if (a.ws_l[s] > 0.0f) mstar = fmaxf(mstar, a.ws_m[s]);
+  }
+  for (int p = 0; p < m.parts; ++p) {
+    const size_t s = (size_t)(m.sb + p) * m.TQ + m.r;
+    const float l = a.ws_l[s];
+    if (l > 0.0f) den += __builtin_amdgcn_exp2f(a.ws_m[s] - mstar) * l;
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  for (int qi = q0; qi < kCols / 4; qi += qstep) {
+    const int c = blockIdx.y * kCols + qi * 4;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int p = 0; p < m.parts; ++p) {
+      const size_t s = (size_t)(m.sb + p) * m.TQ + m.r;
+      const float l = a.ws_l[s];
+      const float w = l > 0.0f ? __builtin_amdgcn_exp2f(a.ws_m[s] - mstar) * l * inv : 0.0f;
+      const uint32_t* o = a.ws_o + (size_t)(m.sb + p) * (a.d / 2) * m.TQ + (size_t)(c >> 1) * m.TQ + m.r;
+      const uint32_t x0 = o[0], x1 = o[m.TQ];
+      acc[0] += w * __uint_as_float(x0 << 16);
+      acc[1] += w * __uint_as_float(x0 & 0xffff0000u);
+      acc[2] += w * __uint_as_float(x1 << 16);
+      acc[3] += w * __uint_as_float(x1 & 0xffff0000u);
+    }
+    store_quad(m, c, acc);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
-  __shared__ float wgt[kMaxParts][kMaxTq];
   if (a.guard && *a.guard == 0ull) return;
   const int g = blockIdx.x;
   const int parts = a.parts[g];
   if (parts <= 1) return;
   const int h = g / a.n_qtiles_head;
   const int qt = g - h * a.n_qtiles_head;
-  const int bat = h / a.heads;
-  const size_t head_off = (size_t)bat * a.batch_stride + (size_t)(h - bat * a.heads) * a.head_stride;
-  const int sb = a.slot_base[g];
-  const int TQ = a.tq;
-  const int D = a.d;
   const int t = threadIdx.x;
-  // (1) per-row common maximum and normalizer; weights of the first kMaxParts
-  // partitions go to LDS, further ones are recomputed while streaming
-  float mstar = -INFINITY, inv = 0.0f;
-  if (t < TQ) {
-#pragma unroll 4
-    for (int p = 0; p < parts; ++p) {
-      const size_t s = (size_t)(sb + p) * TQ + t;
-      if (a.ws_l[s] > 0.0f) mstar = fmaxf(mstar, a.ws_m[s]);
-    }
-    float den = 0.0f;
-#pragma unroll 4
-    for (int p = 0; p < parts; ++p) {
-      const size_t s = (size_t)(sb + p) * TQ + t;
-      const float l = a.ws_l[s];
-      const float w = l > 0.0f ? __builtin_amdgcn_exp2f(a.ws_m[s] - mstar) : 0.0f;
-      den += w * l;
-      if (p < kMaxParts) wgt[p][t] = w * l;  // the partials are normalized by their own l
-    }
-    inv = den > 0.0f ? 1.0f / den : 0.0f;
-    for (int p = 0; p < min(parts, kMaxParts); ++p) wgt[p][t] *= inv;
-  }
-  __syncthreads();
-  // (2) out[r][c..c+3] = sum_p wgt[p][r] * O_p[c..c+3][r] (O_p normalized,
-  // stored as bf16 pairs), c in this workgroup's kCols columns; the
-  // partition loop is unrolled so several partitions' loads are in flight
-  // together
-  const int nitems = TQ * (kCols / 4);
-  for (int item = t; item < nitems; item += 256) {
-    const int r = item % TQ;
-    const int c = blockIdx.y * kCols + (item / TQ) * 4;
-    const int row = qt * TQ + r;
-    if (row >= a.N) continue;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-    for (int p = 0; p < parts; ++p) {
-      float w;
-      if (p < kMaxParts) {
-        w = wgt[p][r];
-      } else {  // recompute (rare: more than kMaxParts partitions)
-        float ms = -INFINITY, den = 0.0f;
-        for (int q = 0; q < parts; ++q) {
-          const size_t s = (size_t)(sb + q) * TQ + r;
-          if (a.ws_l[s] > 0.0f) ms = fmaxf(ms, a.ws_m[s]);
-        }
-        for (int q = 0; q < parts; ++q) {
-          const size_t s = (size_t)(sb + q) * TQ + r;
-          if (a.ws_l[s] > 0.0f) den += __builtin_amdgcn_exp2f(a.ws_m[s] - ms) * a.ws_l[s];
-        }
-        const size_t s = (size_t)(sb + p) * TQ + r;
-        const float l = a.ws_l[s];
-        w = (l > 0.0f && den > 0.0f) ? __builtin_amdgcn_exp2f(a.ws_m[s] - ms) * l / den : 0.0f;
-      }
-      const uint32_t* o = a.ws_o + (size_t)(sb + p) * (D / 2) * TQ + (size_t)(c >> 1) * TQ + r;
-      const uint32_t x0 = o[0], x1 = o[TQ];  // columns (c, c+1) and (c+2, c+3)
-      acc[0] += w * __uint_as_float(x0 << 16);
-      acc[1] += w * __uint_as_float(x0 & 0xffff0000u);
-      acc[2] += w * __uint_as_float(x1 << 16);
-      acc[3] += w * __uint_as_float(x1 & 0xffff0000u);
-    }
-    __bf16 ov[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc[i];
-    *reinterpret_cast<uint2*>(a.o + head_off + (size_t)row * a.row_stride + c) =
-        *reinterpret_cast<const uint2*>(ov);
-  }
+  MergeRow m;
+  m.a = &a;
+  m.sb = a.slot_base[g];
+  m.parts = parts;
+  m.TQ = a.tq;
+  m.r = t % m.TQ;
+  const int row = qt * m.TQ + m.r;
+  if (row >= a.N) return;
+  const int bat = h / a.heads;
+  m.o_row = (size_t)bat * a.batch_stride + (size_t)(h - bat * a.heads) * a.head_stride + (size_t)row * a.row_stride;
+  const int q0 = t / m.TQ, qstep = 256 / m.TQ;  // this thread's 4-column quads of the 16
+  if (parts <= 2) merge_row<2>(m, q0, qstep);
+  else if (parts <= 4) merge_row<4>(m, q0, qstep);
+  else if (parts <= 8) merge_row<8>(m, q0, qstep);
+  else if (parts <= 16) merge_row<16>(m, q0, qstep);
+  else merge_row_any(m, q0, qstep);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s) {
-  if (a.tq > kMaxTq) return hipErrorInvalidValue;
+  if (a.tq > kMaxTq || 256 % a.tq != 0) return hipErrorInvalidValue;
   if (a.d % kCols) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_merge, dim3(n_qtiles, a.d / kCols), dim3(256), 0, s, a);
   return hipGetLastError();
