@@ -162,6 +162,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // with at most 128 queries run three waves per SIMD.
 template <int TQ, int TKV, int D>
 constexpr bool use_w3() { return TKV == 32 && D == 128 && TQ == 128; }
+// 128x64 tiles at d = 128: registers capped at 256 so two workgroups (two
+// waves per SIMD) fit a CU; uncapped the compiler takes 300 and one fits.
+template <int TQ, int TKV, int D>
+constexpr bool use_w2() { return TKV == 64 && D == 128 && TQ == 128; }
 // K fragments read ahead of their MFMA: deeper where registers allow.
 template <int TQ, int TKV, int D>
 constexpr int kpf_depth() { return use_w3<TQ, TKV, D>() ? 2 : 4; }
@@ -601,9 +605,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   }
 }
 
-// Entry points: the generic kernel, and the one for 32-key tiles at d = 128
-// with at most 128 queries, whose registers are capped at 168 so three waves
-// fit a SIMD (the lower-occupancy schedule measured slower).
+// Entry points: the generic kernel, the one for 32-key tiles at d = 128 with
+// at most 128 queries, whose registers are capped at 168 so three waves fit a
+// SIMD (the lower-occupancy schedule measured slower), and the one for 128x64
+// tiles at d = 128, capped at 256 for two waves per SIMD (no spills).
 template <int TQ, int TKV, int D, bool STREAM>
 __global__ __launch_bounds__(TQ * 2) void attn_fwd_kernel(const AttnArgs a) {
   attn_fwd_body<TQ, TKV, D, STREAM>(a);
@@ -614,9 +619,16 @@ __attribute__((amdgpu_num_vgpr(168))) void attn_fwd_kernel_w3(const AttnArgs a) 
   attn_fwd_body<TQ, TKV, D, STREAM>(a);
 }
 template <int TQ, int TKV, int D, bool STREAM>
+__global__ __launch_bounds__(TQ * 2) __attribute__((amdgpu_waves_per_eu(2)))
+__attribute__((amdgpu_num_vgpr(256))) void attn_fwd_kernel_w2(const AttnArgs a) {
+  attn_fwd_body<TQ, TKV, D, STREAM>(a);
+}
+template <int TQ, int TKV, int D, bool STREAM>
 void launch_attn_as(const AttnArgs& a, int grid, hipStream_t s) {
   if constexpr (use_w3<TQ, TKV, D>())
     hipLaunchKernelGGL((attn_fwd_kernel_w3<TQ, TKV, D, STREAM>), dim3(grid), dim3(TQ * 2), 0, s, a);
+  else if constexpr (use_w2<TQ, TKV, D>())
+    hipLaunchKernelGGL((attn_fwd_kernel_w2<TQ, TKV, D, STREAM>), dim3(grid), dim3(TQ * 2), 0, s, a);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<TQ, TKV, D, STREAM>), dim3(grid), dim3(TQ * 2), 0, s, a);
 }

@@ -30,6 +30,8 @@ static int wg_per_cu_as() {
   hipError_t e;
   if constexpr (use_w3<TQ, TKV, D>())
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel_w3<TQ, TKV, D, STREAM>, TQ * 2, 0);
+  else if constexpr (use_w2<TQ, TKV, D>())
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel_w2<TQ, TKV, D, STREAM>, TQ * 2, 0);
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel<TQ, TKV, D, STREAM>, TQ * 2, 0);
   return e == hipSuccess ? n : 0;
