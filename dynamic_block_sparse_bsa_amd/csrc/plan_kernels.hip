@@ -223,12 +223,131 @@ __global__ __launch_bounds__(256) void k_compact(const uint8_t* __restrict__ mas
   }
 }
 
+// Row bits of a 16-byte aligned mask, 16 columns per lane: the row's bytes
+// [start, start + nkb) are covered by the aligned 16-byte chunks from a0 =
+// start & ~15; window w holds chunks a0 + 1024 w + 16 l (lane l).  Bit i of a
+// lane's value is byte (chunk + i) != 0, with bytes outside the row cleared.
+// A chunk that would cross the end of the mask buffer is read bytewise.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t nz_bits16(const u32x4v x);
+
+__device__ inline uint32_t row_chunk_bits(const uint8_t* __restrict__ mask, size_t total, size_t start,
+                                          int nkb, size_t a0, int w, int lane) {
+  const size_t c = a0 + (size_t)w * 1024 + 16 * (size_t)lane;
+  const size_t end = start + (size_t)nkb;
+  if (c >= end) return 0u;
+  uint32_t m;
+  if (c + 16 <= total) {
+    m = nz_bits16(*reinterpret_cast<const u32x4v*>(mask + c));
+  } else {
+    m = 0u;
+    for (int i = 0; c + i < total; ++i) m |= (uint32_t)(mask[c + i] != 0) << i;
+  }
+  if (c < start) m &= 0xffffu << (unsigned)(start - c);
+  if (c + 16 > end) m &= (1u << (unsigned)(end - c)) - 1u;
+  return m & 0xffffu;
+}
+
+// k_row_count for a 16-byte aligned mask (same outputs): a wave per row reads
+// the row 1 KB per load; run neighbours cross lanes by shuffles and windows
+// by carrying the previous window's last bit and peeking the next window's
+// first.
+__global__ __launch_bounds__(256) void k_row_count16(const uint8_t* __restrict__ mask, int32_t nrows,
+                                                     int32_t nkb, int32_t* __restrict__ row_cnt,
+                                                     RowPartial* __restrict__ part) {
+  __shared__ unsigned long long s_long[4];
+  __shared__ unsigned s_max[4], s_empty[4];
+  const int l = (int)lane_id();
+  const int wv = threadIdx.x >> 6;
+  const size_t total = (size_t)nrows * (size_t)nkb;
+  unsigned long long lng_w = 0;
+  unsigned max_w = 0, empty_w = 0;
+  const int nwaves = gridDim.x * 4;
+  for (int row = blockIdx.x * 4 + wv; row < nrows; row += nwaves) {
+    const size_t start = (size_t)row * (size_t)nkb;
+    const size_t a0 = start & ~(size_t)15;
+    const int nwin = (int)((start + nkb - a0 + 1023) / 1024);
+    unsigned cnt = 0, lng = 0, prevtop = 0u;
+    uint32_t cur = row_chunk_bits(mask, total, start, nkb, a0, 0, l);
+    for (int w = 0; w < nwin; ++w) {
+      const uint32_t nxt = (w + 1 < nwin) ? row_chunk_bits(mask, total, start, nkb, a0, w + 1, l) : 0u;
+      const uint32_t up = (uint32_t)__shfl_up((int)cur, 1, 64);
+      const uint32_t dn = (uint32_t)__shfl_down((int)cur, 1, 64);
+      const uint32_t nxt0 = (uint32_t)__shfl((int)nxt, 0, 64);
+      const uint32_t top = (uint32_t)__shfl((int)cur, 63, 64);
+      const uint32_t lbit = l == 0 ? prevtop : ((up >> 15) & 1u);
+      const uint32_t rbit = l == 63 ? (nxt0 & 1u) : (dn & 1u);
+      const uint32_t left = ((cur << 1) | lbit) & 0xffffu;
+      const uint32_t right = (cur >> 1) | (rbit << 15);
+      cnt += __popc(cur);
+      lng += __popc(cur & (left | right));
+      prevtop = (top >> 15) & 1u;
+      cur = nxt;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      cnt += (unsigned)__shfl_xor((int)cnt, o, 64);
+      lng += (unsigned)__shfl_xor((int)lng, o, 64);
+    }
+    if (l == 0) row_cnt[row] = (int32_t)cnt;
+    lng_w += lng;
+    max_w = max(max_w, cnt);
+    empty_w += (cnt == 0);
+  }
+  if (l == 0) {
+    s_long[wv] = lng_w;
+    s_max[wv] = max_w;
+    s_empty[wv] = empty_w;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    RowPartial rp;
+    rp.long_run = s_long[0] + s_long[1] + s_long[2] + s_long[3];
+    rp.max_row = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+    rp.empty = s_empty[0] + s_empty[1] + s_empty[2] + s_empty[3];
+    part[blockIdx.x] = rp;
+  }
+}
+
+// k_compact for a 16-byte aligned mask (same outputs): a wave per row, 16
+// columns per lane per window, lane offsets by a wave scan of the lanes' bit
+// counts.
+__global__ __launch_bounds__(256) void k_compact16(const uint8_t* __restrict__ mask, int32_t nrows,
+                                                   int32_t nkb, const int32_t* __restrict__ row_ptr,
+                                                   int32_t* __restrict__ cols) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const int l = (int)lane_id();
+  const size_t total = (size_t)nrows * (size_t)nkb;
+  const size_t start = (size_t)row * (size_t)nkb;
+  const size_t a0 = start & ~(size_t)15;
+  const int nwin = (int)((start + nkb - a0 + 1023) / 1024);
+  int32_t out = row_ptr[row];
+  for (int w = 0; w < nwin; ++w) {
+    uint32_t m = row_chunk_bits(mask, total, start, nkb, a0, w, l);
+    const int32_t c = (int32_t)__popc(m);
+    const int32_t incl = wave_scan(c);
+    int32_t o = out + incl - c;
+    const int32_t base = (int32_t)(a0 + (size_t)w * 1024 + 16 * (size_t)l - start);  // column of bit 0
+    while (m) {
+      cols[o++] = base + __ffs(m) - 1;
+      m &= m - 1u;
+    }
+    out += __shfl(incl, 63, 64);
+  }
+}
+
 // Bit i (i < 4) set iff byte i of x is nonzero: per byte, adding 0x7f to
 // its low seven bits sets bit 7 iff they are nonzero (no carry leaves the
 // byte), OR-ing x adds its own bit 7; the four byte flags are then gathered.
 __device__ inline uint32_t nz_bits4(uint32_t x) {
   const uint32_t y = (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
   return ((y >> 7) | (y >> 14) | (y >> 21) | (y >> 28)) & 0xfu;
+}
+
+__device__ inline uint32_t nz_bits16(const u32x4v x) {
+  return nz_bits4(x[0]) | (nz_bits4(x[1]) << 4) | (nz_bits4(x[2]) << 8) | (nz_bits4(x[3]) << 12);
 }
 
 // The whole mask state of a small mask in one launch (one workgroup of 1024):
@@ -764,8 +883,12 @@ int row_count_blocks(int32_t nrows) { return std::max(1, std::min((nrows + 3) / 
 
 hipError_t launch_row_count(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_cnt,
                             RowPartial* part, hipStream_t s) {
-  hipLaunchKernelGGL(k_row_count, dim3(row_count_blocks(nrows)), dim3(256), 0, s, mask, nrows, nkb,
-                     row_cnt, part);
+  if (((uintptr_t)mask & 15) == 0)
+    hipLaunchKernelGGL(k_row_count16, dim3(row_count_blocks(nrows)), dim3(256), 0, s, mask, nrows, nkb,
+                       row_cnt, part);
+  else
+    hipLaunchKernelGGL(k_row_count, dim3(row_count_blocks(nrows)), dim3(256), 0, s, mask, nrows, nkb,
+                       row_cnt, part);
   return hipGetLastError();
 }
 
@@ -791,8 +914,11 @@ hipError_t launch_mask_small(const uint8_t* mask, int32_t nrows, int32_t nkb, in
 
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
                           int32_t* cols, hipStream_t s) {
-  hipLaunchKernelGGL(k_compact, dim3((nrows + 3) / 4), dim3(256), 0, s, mask, nrows, nkb, row_ptr,
-                     cols);
+  if (((uintptr_t)mask & 15) == 0)
+    hipLaunchKernelGGL(k_compact16, dim3((nrows + 3) / 4), dim3(256), 0, s, mask, nrows, nkb, row_ptr, cols);
+  else
+    hipLaunchKernelGGL(k_compact, dim3((nrows + 3) / 4), dim3(256), 0, s, mask, nrows, nkb, row_ptr,
+                       cols);
   return hipGetLastError();
 }
 
