@@ -191,7 +191,7 @@ def run(cases, make_mask, reps=5, warmup=2, log=print):
         shape = (cat[sel]["tile_q"], cat[sel]["tile_kv"], cat[sel]["d"])
         same = {pid: t for pid, t in lat.items()
                 if (cat[pid]["tile_q"], cat[pid]["tile_kv"], cat[pid]["d"]) == shape}
-        o0 = [pid for pid in same if cat[pid]["split"] == 1 and cat[pid]["xcd_remap"] == 0
+        o0 = [pid for pid in same if cat[pid]["split"] == 2 and cat[pid]["xcd_remap"] == 0
               and cat[pid]["order"] == 0]
         row = dict(block=list(block), H=H, N=N, d=d, family=c["family"], density=info["density"],
                    run_coverage=info["run_coverage"], row_skew=info["row_skew"],

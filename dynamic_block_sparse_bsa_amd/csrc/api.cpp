@@ -190,7 +190,7 @@ int wg_per_cu_cached(int tq, int tkv, int d, bool stream = false) {
 }
 
 // Split-K rule of the "balance" organizations: a query tile's traversal is cut
-// when it holds more entries than 1/split of the even share of all entries
+// when it holds more entries than 2/split of the even share of all entries
 // over the resident workgroup slots of the device (at least 4 entries per
 // partition).
 struct PlanShape {
@@ -227,7 +227,7 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
     split = r.force_split;
   } else if (r.force_split < 0 && e.split) {
     const int64_t slots = (int64_t)device_cus(dev) * wg_per_cu_cached(e.tq, e.tkv, e.d);
-    split = (int)std::max<int64_t>(4, cdiv(std::max<int64_t>(W, 1), slots * e.split));
+    split = (int)std::max<int64_t>(4, cdiv(2 * std::max<int64_t>(W, 1), slots * e.split));
     if (row_max <= split) split = 0;
   }
   p.split = split;

@@ -28,11 +28,12 @@ std::vector<CatalogEntry> build_catalog() {
                                  {256, 64, 64}};
   std::vector<CatalogEntry> c;
   for (const Shape& s : shapes) {
-    // organizations {split, XCD runs, order}: split-K balance rule; no split;
+    // organizations {split, XCD runs, order} (split in halves: partitions of
+    // at most 2/split of the even share): split-K balance rule; no split;
     // split-K + runs of kXcdRun consecutive tasks per XCD; longest-first task
-    // order without split, with the balance rule, and with partitions of half
-    // the balance rule's share
-    const int orgs[][3] = {{1, 0, 0}, {0, 0, 0}, {1, kXcdRun, 0}, {0, 0, 1}, {1, 0, 1}, {2, 0, 1}};
+    // order without split, with the balance rule, with partitions of half the
+    // balance rule's share, and of two thirds of it
+    const int orgs[][3] = {{2, 0, 0}, {0, 0, 0}, {2, kXcdRun, 0}, {0, 0, 1}, {2, 0, 1}, {4, 0, 1}, {3, 0, 1}};
     for (auto& o : orgs) {
       CatalogEntry e;
       e.id = (int)c.size();
@@ -44,7 +45,7 @@ std::vector<CatalogEntry> build_catalog() {
       e.order = o[2];
       char buf[48];
       std::snprintf(buf, sizeof buf, "T%dx%d_d%d_%s%s%s", e.tq, e.tkv, e.d,
-                    e.split == 0 ? "nosplit" : e.split == 1 ? "splitk" : "splitk2",
+                    e.split == 0 ? "nosplit" : e.split == 2 ? "splitk" : e.split == 3 ? "splitk15" : "splitk2",
                     e.xcd_remap ? "_xcd" : "", e.order ? "_lpt" : "");
       e.name = buf;
       c.push_back(e);
@@ -161,12 +162,12 @@ bool eligible(const CatalogEntry& e, const bsa_request& r, int64_t ws_bytes, std
 int base_plan(const bsa_request& r) {
   const auto& c = catalog();
   for (auto& e : c)
-    if (e.tq == r.block_q && e.tkv == r.block_kv && e.d == r.d && e.split == 1 && e.xcd_remap == 0 &&
+    if (e.tq == r.block_q && e.tkv == r.block_kv && e.d == r.d && e.split == 2 && e.xcd_remap == 0 &&
         e.order == 0 && eligible(e, r, -1, nullptr))
       return e.id;
   int best = -1;
   for (auto& e : c) {
-    if (e.split != 1 || e.xcd_remap != 0 || e.order != 0 || !eligible(e, r, -1, nullptr)) continue;
+    if (e.split != 2 || e.xcd_remap != 0 || e.order != 0 || !eligible(e, r, -1, nullptr)) continue;
     if (best < 0 || e.tq * e.tkv < c[best].tq * c[best].tkv) best = e.id;
   }
   return best;

@@ -25,7 +25,7 @@ struct CatalogEntry {
   int id;
   int tq, tkv, d;
   int split;      // 0: one task per query tile; s >= 1: balance rule with
-                  // partitions of at most 1/s of the even share per slot
+                  // partitions of at most 2/s of the even share per slot
   int xcd_remap;  // > 0: runs of this many consecutive tasks per XCD
   int order;      // 0: tasks in query-tile order; 1: longest first
   std::string name;

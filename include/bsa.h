@@ -116,7 +116,7 @@ typedef struct {
   int32_t id;
   int32_t tile_q, tile_kv, d;
   int32_t split;        /* 0 = never split; s >= 1 = balance rule, partitions of
-                           at most 1/s of the even share of entries per slot   */
+                           at most 2/s of the even share of entries per slot   */
   int32_t xcd_remap;    /* > 0: runs of this many consecutive tasks per XCD      */
   int32_t order;        /* 0 = query-tile order, 1 = longest task first          */
   char name[48];

@@ -149,7 +149,7 @@ def test_stream_organization(block, N, H):
     ref = oatt.attention_rows(q, k, v, M, block[0], block[1], rows)
     checked = 0
     for e in bsa.catalog():
-        if e["order"] != 0 or e["xcd_remap"] != 0 or e["split"] != 1 or not bsa.eligible(e["id"], H, N, d, block):
+        if e["order"] != 0 or e["xcd_remap"] != 0 or e["split"] != 2 or not bsa.eligible(e["id"], H, N, d, block):
             continue
         p = bsa.plan(Md, block, H, N, d, force_plan=e["id"], force_split=bsa.SPLIT_STREAM)
         info = p.info

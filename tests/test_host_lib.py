@@ -29,7 +29,7 @@ def test_catalog_and_hash():
     shapes = {(e["tile_q"], e["tile_kv"], e["d"]) for e in cat}
     orgs = {(e["split"], e["xcd_remap"], e["order"]) for e in cat}
     assert len(cat) == len(shapes) * len(orgs)  # every organization of every kernel shape
-    assert {(1, 0, 0), (0, 0, 0), (1, 0, 1), (2, 0, 1), (0, 0, 1)} <= orgs
+    assert {(2, 0, 0), (0, 0, 0), (2, 0, 1), (3, 0, 1), (4, 0, 1), (0, 0, 1)} <= orgs
     names = [e["name"] for e in cat]
     assert len(set(names)) == len(names)
     assert re.fullmatch(r"[0-9a-f]{16}", bsa.catalog_hash())
@@ -39,7 +39,7 @@ def test_base_plan_direct_or_smallest_refined():
     cat = {e["id"]: e for e in bsa.catalog()}
     e = cat[bsa.base_plan(8, 8192, 128, (128, 128))]
     assert (e["tile_q"], e["tile_kv"]) == (128, 128)  # Direct when the catalog has T = B
-    assert e["split"] == 1 and e["xcd_remap"] == 0 and e["order"] == 0  # default organization
+    assert e["split"] == 2 and e["xcd_remap"] == 0 and e["order"] == 0  # default organization
     e = cat[bsa.base_plan(24, 115200, 128, (32, 128))]
     assert e["tile_q"] * e["tile_kv"] == min(
         c["tile_q"] * c["tile_kv"] for c in cat.values()
@@ -74,10 +74,10 @@ def test_eligibility_rules():
     by = {(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"]): e["id"] for e in cat
           if e["order"] == 0}
     # coarsening B_Q = 16 into a 64-row tile would split a wave across logical rows
-    assert not bsa.eligible(by[(64, 64, 128, 1, 0)], 1, 1024, 128, (16, 64))
-    assert bsa.eligible(by[(64, 64, 128, 1, 0)], 1, 1024, 128, (32, 64))
-    assert not bsa.eligible(by[(64, 64, 128, 1, 0)], 1, 1024, 64, (64, 64))  # head dim
-    assert bsa.eligible(by[(128, 32, 128, 1, 0)], 1, 1024, 128, (64, 128))  # mixed map
+    assert not bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 128, (16, 64))
+    assert bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 128, (32, 64))
+    assert not bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 64, (64, 64))  # head dim
+    assert bsa.eligible(by[(128, 32, 128, 2, 0)], 1, 1024, 128, (64, 128))  # mixed map
 
 
 def test_unsupported_request_errors():
