@@ -145,10 +145,13 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
                           int32_t nkb, int32_t cq, int32_t ckv, int32_t ntr, int32_t ntc,
                           int32_t* trow_cnt, const int32_t* trow_ptr, int32_t* tcol,
                           uint32_t* tbits, hipStream_t s);
+// dev_split >= 0: split and max_len are derived on the device from *st (the
+// balance rule with split share dev_split in halves over `slots` workgroups,
+// uncoarsened tile list); -1: the given split and max_len are used.
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
-                        hipStream_t s);
+                        hipStream_t s, int32_t dev_split = -1, int32_t slots = 0);
 hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s);
 
 // Attention kernel table: returns nullptr when (tq, tkv, d) has no kernel.

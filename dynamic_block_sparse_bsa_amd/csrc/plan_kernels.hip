@@ -599,16 +599,35 @@ __device__ inline Task make_task(const RowTasks& r, int i, int slot0) {
   return tk;
 }
 
+//
+// dev_split >= 0: split and max_len are not given but derived here from the
+// statistics in *st with the host's balance rule for a plan of split share
+// dev_split (in halves; 0 = never split) over `slots` resident workgroups
+// and an uncoarsened tile list, so the builder can be queued before the host
+// has read the statistics.
 __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow_ptr, int32_t H,
                                                 int32_t nqt_head, int32_t ntr, int32_t refine_q,
                                                 int32_t split, int32_t order, int32_t max_len,
                                                 int32_t* __restrict__ parts,
                                                 int32_t* __restrict__ slot_base,
-                                                Task* __restrict__ tasks, MaskStats* st) {
+                                                Task* __restrict__ tasks, MaskStats* st,
+                                                int32_t dev_split, int32_t slots) {
   __shared__ int32_t lds[32];
   __shared__ int32_t cursor[kLenBuckets];
   const int t = threadIdx.x;
   const int nqt = H * nqt_head;
+  if (dev_split >= 0) {
+    const long long W = (long long)refine_q * (long long)st->nnz;
+    const long long row_max = (long long)st->max_row_nnz;
+    long long sp = 0;
+    if (dev_split > 0) {
+      const long long den = (long long)slots * dev_split;
+      sp = max(4LL, (2 * max(W, 1LL) + den - 1) / den);
+      if (row_max <= sp) sp = 0;
+    }
+    split = (int32_t)sp;
+    max_len = sp > 0 ? (int32_t)sp : (int32_t)min(row_max, (long long)(1 << 30));
+  }
   max_len = max(max_len, 1);
   if (order) cursor[t] = 0;
   __syncthreads();
@@ -945,9 +964,9 @@ hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_h
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t dev_split, int32_t slots) {
   hipLaunchKernelGGL(k_tasks, dim3(1), dim3(1024), 0, s, trow_ptr, H, nqt_head, ntr, refine_q, split,
-                     order, max_len, parts, slot_base, tasks, st);
+                     order, max_len, parts, slot_base, tasks, st, dev_split, slots);
   return hipGetLastError();
 }
 

@@ -109,6 +109,10 @@ typedef struct {
   double run_coverage;  /* long_run_blocks / active, 0 for an empty mask        */
   double row_skew;      /* max_row_nnz * rows / active blocks (>= 1), 0 if empty */
   double host_select_us;   /* host time spent in regime lookup + ranking scan   */
+  int32_t tasks_predicted; /* 1: the task list was built speculatively for the
+                              entry this request key selected last time, queued
+                              before the statistics reached the host, and the
+                              selection agreed; 0: built after the selection */
 } bsa_plan_info;
 
 /* Description of one catalog entry (paper section 4.4: native catalog). */
