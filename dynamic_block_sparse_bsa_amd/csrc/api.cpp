@@ -285,7 +285,7 @@ struct bsa_plan {
   MaskStats stats{};
   bsa_plan_info info{};
   DevBuf stats_dev, row_cnt, row_ptr, row_part, cols, trow_cnt, trow_ptr_buf, tcol_buf, tbits_buf, parts,
-      slot_off, tasks, ws, seg_ptr, spec_parts, spec_slot, spec_tasks;
+      slot_off, tasks, ws, seg_ptr, spec_parts, spec_slot, spec_tasks, split_tiles, spec_split;
   const int32_t* trow_ptr = nullptr;
   const int32_t* tcol = nullptr;
   const uint32_t* tbits = nullptr;
@@ -295,7 +295,7 @@ struct bsa_plan {
 
   ~bsa_plan() {
     for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &row_part, &cols, &trow_cnt, &trow_ptr_buf, &tcol_buf,
-                      &tbits_buf, &parts, &slot_off, &tasks, &ws, &seg_ptr, &spec_parts, &spec_slot, &spec_tasks})
+                      &tbits_buf, &parts, &slot_off, &tasks, &ws, &seg_ptr, &spec_parts, &spec_slot, &spec_tasks, &split_tiles, &spec_split})
       pool_release(b);
     for (auto& e : ev) event_put(dev, true, e);
     event_put(dev, false, done);
@@ -695,9 +695,11 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     if ((err = pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->spec_slot)) != hipSuccess) return err;
     if ((err = pool_alloc(p->dev, sizeof(Task) * (size_t)std::max<int64_t>(cap, 1), &p->spec_tasks)) != hipSuccess)
       return err;
+    if (dev_split > 0 && (err = pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->spec_split)) != hipSuccess)
+      return err;
     err = launch_tasks((const int32_t*)p->row_ptr.ptr, r.H, nqt_head, p->nqb, mq.refine, 0, e.order, 0,
                        (int32_t*)p->spec_parts.ptr, (int32_t*)p->spec_slot.ptr, (Task*)p->spec_tasks.ptr, dst, s,
-                       dev_split, (int32_t)slots);
+                       dev_split, (int32_t)slots, (int32_t*)p->spec_split.ptr);
     spec_launched = err == hipSuccess;
     return err;
   };
@@ -828,10 +830,12 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     std::swap(p->parts, p->spec_parts);
     std::swap(p->slot_off, p->spec_slot);
     std::swap(p->tasks, p->spec_tasks);
+    std::swap(p->split_tiles, p->spec_split);
   } else {
+    if (shape.split > 0) HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->split_tiles));
     HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split, chosen->order,
                          (int32_t)max_len, (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr,
-                         (Task*)p->tasks.ptr, dst, s));
+                         (Task*)p->tasks.ptr, dst, s, -1, 0, (int32_t*)p->split_tiles.ptr));
   }
   pred_store(pkey, predictable(*chosen, r) && shape.groups == 0 ? chosen->id : -1);
   if (shape.slots_upper > 0) HIP_TRY(pool_alloc(p->dev, (size_t)shape.ws_bytes, &p->ws));
@@ -943,7 +947,15 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
     m.n_qtiles_head = p->shape.nqt_head;
     m.tq = e.tq;
     m.d = e.d;
-    HIP_TRY(launch_merge(m, (int32_t)p->shape.nqt, s));
+    // with the builder's list of split tiles, a fixed grid loops over their
+    // items (most query tiles are not split)
+    int32_t grid_items = 0;
+    if (p->split_tiles.ptr && p->shape.groups == 0) {
+      m.split_tiles = (const int32_t*)p->split_tiles.ptr;
+      m.n_split = &((const MaskStats*)p->stats_dev.ptr)->n_split;
+      grid_items = (int32_t)std::min<int64_t>(p->shape.nqt * (e.d / kMergeCols), 8LL * device_cus(p->dev));
+    }
+    HIP_TRY(launch_merge(m, (int32_t)p->shape.nqt, s, grid_items));
   }
   if (!timed) {
     HIP_TRY(hipEventRecord(mp->done, s));

@@ -29,6 +29,7 @@ struct MaskStats {
   unsigned int max_row_nnz;          // largest active count of a query-block row
   unsigned int empty_rows;           // query-block rows with no active block
   unsigned long long n_tasks;        // tasks written by the task builder
+  unsigned long long n_split;        // query tiles with more than one partition
   unsigned long long seq;            // host copy: request sequence number, written last
 };
 
@@ -106,6 +107,11 @@ struct MergeArgs {
   const float* ws_m;
   const float* ws_l;
   const uint32_t* ws_o;     // [slot][d/2][T_Q] bf16 pairs, normalized partials
+  // Optional compact list of the split query tiles (ascending) and its
+  // device count; the launch then loops over (listed tile, column group)
+  // items instead of one workgroup per (tile, column group).
+  const int32_t* split_tiles;
+  const unsigned long long* n_split;
   int32_t N;
   int32_t n_qtiles_head;    // query tiles per head
   int32_t tq;
@@ -148,11 +154,18 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
 // dev_split >= 0: split and max_len are derived on the device from *st (the
 // balance rule with split share dev_split in halves over `slots` workgroups,
 // uncoarsened tile list); -1: the given split and max_len are used.
+// split_tiles (nullable): receives the query tiles with more than one
+// partition, ascending; their count goes to st->n_split.
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
-                        hipStream_t s, int32_t dev_split = -1, int32_t slots = 0);
-hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s);
+                        hipStream_t s, int32_t dev_split = -1, int32_t slots = 0,
+                        int32_t* split_tiles = nullptr);
+// With a.split_tiles, grid_items (> 0) workgroups loop over the listed
+// (tile, column group) items; otherwise one workgroup per (query tile,
+// column group).  A column group is kMergeCols output columns.
+constexpr int kMergeCols = 16;
+hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s, int32_t grid_items = 0);
 
 // Attention kernel table: returns nullptr when (tq, tkv, d) has no kernel.
 AttnLauncher attn_launcher(int tq, int tkv, int d);

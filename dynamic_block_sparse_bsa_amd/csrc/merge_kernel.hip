@@ -20,11 +20,12 @@ namespace bsa {
 namespace {
 
 constexpr int kMaxTq = 256;
-constexpr int kCols = 16;       // output columns per workgroup
+constexpr int kCols = kMergeCols;  // output columns per item
 
 struct MergeRow {
   const MergeArgs* a;
   int sb, parts, TQ, r;
+  int c0;        // first output column of the item's column group
   size_t o_row;  // output element offset of the row
 };
 
@@ -68,7 +69,7 @@ __device__ __forceinline__ void merge_row(const MergeRow& m, int q0, int qstep) 
   float w[P];
   row_weights<P>(m, w);
   for (int qi = q0; qi < kCols / 4; qi += qstep) {
-    const int c = blockIdx.y * kCols + qi * 4;
+    const int c = m.c0 + qi * 4;
     uint32_t x0[P], x1[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -105,7 +106,7 @@ __device__ void merge_row_any(const MergeRow& m, int q0, int qstep) {
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   for (int qi = q0; qi < kCols / 4; qi += qstep) {
-    const int c = blockIdx.y * kCols + qi * 4;
+    const int c = m.c0 + qi * 4;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
     for (int p = 0; p < m.parts; ++p) {
@@ -123,9 +124,8 @@ __device__ void merge_row_any(const MergeRow& m, int q0, int qstep) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
-  if (a.guard && *a.guard == 0ull) return;
-  const int g = blockIdx.x;
+// One (query tile g, column group cg) item: this thread's row of the tile.
+__device__ __forceinline__ void merge_item(const MergeArgs& a, int g, int cg) {
   const int parts = a.parts[g];
   if (parts <= 1) return;
   const int h = g / a.n_qtiles_head;
@@ -137,11 +137,12 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   m.parts = parts;
   m.TQ = a.tq;
   m.r = t % m.TQ;
+  m.c0 = cg * kCols;
   const int row = qt * m.TQ + m.r;
   if (row >= a.N) return;
   const int bat = h / a.heads;
   m.o_row = (size_t)bat * a.batch_stride + (size_t)(h - bat * a.heads) * a.head_stride + (size_t)row * a.row_stride;
-  const int q0 = t / m.TQ, qstep = 256 / m.TQ;  // this thread's 4-column quads of the 16
+  const int q0 = t / m.TQ, qstep = 256 / m.TQ;  // this thread's 4-column quads of the group
   if (parts <= 2) merge_row<2>(m, q0, qstep);
   else if (parts <= 4) merge_row<4>(m, q0, qstep);
   else if (parts <= 8) merge_row<8>(m, q0, qstep);
@@ -149,12 +150,31 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   else merge_row_any(m, q0, qstep);
 }
 
+// Grid (query tiles, column groups), or with the compact list of split tiles
+// a fixed number of workgroups looping over (listed tile, column group)
+// items (no barrier, so a workgroup's threads need not stay in step).
+__global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
+  if (a.guard && *a.guard == 0ull) return;
+  if (a.split_tiles) {
+    const int ng = a.d / kCols;
+    const long long items = (long long)(*a.n_split) * ng;
+    for (long long it = blockIdx.x; it < items; it += gridDim.x)
+      merge_item(a, a.split_tiles[it / ng], (int)(it % ng));
+  } else {
+    merge_item(a, blockIdx.x, blockIdx.y);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s) {
+hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s, int32_t grid_items) {
   if (a.tq > kMaxTq || 256 % a.tq != 0) return hipErrorInvalidValue;
   if (a.d % kCols) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_merge, dim3(n_qtiles, a.d / kCols), dim3(256), 0, s, a);
+  if (a.split_tiles) {
+    if (grid_items <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_merge, dim3(grid_items), dim3(256), 0, s, a);
+  } else
+    hipLaunchKernelGGL(k_merge, dim3(n_qtiles, a.d / kCols), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ __device__ inline void publish_stats(MaskStats* h, const MaskStats& r) {
   sys_store(&h->max_row_nnz, r.max_row_nnz);
   sys_store(&h->empty_rows, r.empty_rows);
   sys_store(&h->n_tasks, 0ull);
+  sys_store(&h->n_split, 0ull);
   sys_publish_seq(&h->seq, r.seq);
 }
 
@@ -197,6 +198,7 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
       r.max_row_nnz = s_max[0];
       r.empty_rows = s_empty[0];
       r.n_tasks = 0;
+      r.n_split = 0;
       r.seq = seq;
       *st = r;
       // fine-grained host memory, read by the host while this stream runs on
@@ -457,6 +459,7 @@ __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__
       r.empty_rows += s_empty[w];
     }
     r.n_tasks = 0;
+    r.n_split = 0;
     r.seq = seq;
     *st = r;
     if (host_st) publish_stats(host_st, r);
@@ -611,7 +614,8 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
                                                 int32_t* __restrict__ parts,
                                                 int32_t* __restrict__ slot_base,
                                                 Task* __restrict__ tasks, MaskStats* st,
-                                                int32_t dev_split, int32_t slots) {
+                                                int32_t dev_split, int32_t slots,
+                                                int32_t* __restrict__ split_tiles) {
   __shared__ int32_t lds[32];
   __shared__ int32_t cursor[kLenBuckets];
   const int t = threadIdx.x;
@@ -633,7 +637,7 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
   __syncthreads();
   // pass 1: partition counts and workspace slots in query-tile order; the
   // tasks themselves (query-tile order) or their length histogram
-  int32_t carry_t = 0, carry_s = 0;
+  int32_t carry_t = 0, carry_s = 0, carry_x = 0;
   RowTasks keep[4];  // a single chunk's rows and slot offset, reused by pass 2
   int32_t keep_off_s = 0;
   for (int base = 0; base < nqt; base += 4096) {
@@ -653,6 +657,16 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
     int32_t off_t = carry_t + block_scan(sum_t, lds, &tot_t);
     int32_t off_s = carry_s + block_scan(sum_s, lds, &tot_s);
     keep_off_s = off_s;
+    if (split_tiles) {
+      int32_t nsp = 0, tot_x;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) nsp += r[k].p > 1;
+      int32_t off_x = carry_x + block_scan(nsp, lds, &tot_x);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (r[k].p > 1) split_tiles[off_x++] = g0 + k;
+      carry_x += tot_x;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) keep[k] = r[k];
 #pragma unroll
@@ -675,7 +689,10 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
     carry_t += tot_t;
     carry_s += tot_s;
   }
-  if (t == 0) st->n_tasks = (unsigned long long)carry_t;
+  if (t == 0) {
+    st->n_tasks = (unsigned long long)carry_t;
+    st->n_split = (unsigned long long)carry_x;
+  }
   if (!order) return;
   // bucket starts, then pass 2 places every task at its bucket's cursor
   __syncthreads();
@@ -964,9 +981,9 @@ hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_h
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
-                        hipStream_t s, int32_t dev_split, int32_t slots) {
+                        hipStream_t s, int32_t dev_split, int32_t slots, int32_t* split_tiles) {
   hipLaunchKernelGGL(k_tasks, dim3(1), dim3(1024), 0, s, trow_ptr, H, nqt_head, ntr, refine_q, split,
-                     order, max_len, parts, slot_base, tasks, st, dev_split, slots);
+                     order, max_len, parts, slot_base, tasks, st, dev_split, slots, split_tiles);
   return hipGetLastError();
 }
 
