@@ -679,7 +679,10 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   const PredKey pkey = pred_key(p->dev, r);
   const int pred_id = pred_lookup(pkey);
   bool spec_launched = false;
-  auto launch_spec_tasks = [&]() -> hipError_t {
+  // Allocates the speculative buffers and fills `ts` (ts.enabled stays 0
+  // when there is no usable prediction).
+  auto prepare_spec = [&](TaskSpec& ts) -> hipError_t {
+    ts = TaskSpec{};
     if (pred_id < 0 || pred_id >= (int)catalog().size()) return hipSuccess;
     const CatalogEntry& e = catalog()[pred_id];
     if (!predictable(e, r) || !attn_launcher(e.tq, e.tkv, e.d)) return hipSuccess;
@@ -697,11 +700,19 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
       return err;
     if (dev_split > 0 && (err = pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->spec_split)) != hipSuccess)
       return err;
-    err = launch_tasks((const int32_t*)p->row_ptr.ptr, r.H, nqt_head, p->nqb, mq.refine, 0, e.order, 0,
-                       (int32_t*)p->spec_parts.ptr, (int32_t*)p->spec_slot.ptr, (Task*)p->spec_tasks.ptr, dst, s,
-                       dev_split, (int32_t)slots, (int32_t*)p->spec_split.ptr);
-    spec_launched = err == hipSuccess;
-    return err;
+    ts.enabled = 1;
+    ts.H = r.H;
+    ts.nqt_head = nqt_head;
+    ts.ntr = p->nqb;
+    ts.refine_q = mq.refine;
+    ts.order = e.order;
+    ts.dev_split = dev_split;
+    ts.slots = (int32_t)slots;
+    ts.parts = (int32_t*)p->spec_parts.ptr;
+    ts.slot_base = (int32_t*)p->spec_slot.ptr;
+    ts.tasks = (Task*)p->spec_tasks.ptr;
+    ts.split_tiles = (int32_t*)p->spec_split.ptr;
+    return hipSuccess;
   };
   thread_local unsigned long long seq = 0;  // the host statistics buffer is per thread
   ++seq;
@@ -711,9 +722,12 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     // small mask: counts, statistics, scan and compaction in one launch
     early_compact = true;
     HIP_TRY(pool_alloc(p->dev, cols_bound, &p->cols));
+    // (with a prediction, the same kernel also builds the speculative list)
+    TaskSpec ts;
+    HIP_TRY(prepare_spec(ts));
     HIP_TRY(launch_mask_small(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, dst, host,
-                              seq, s));
-    HIP_TRY(launch_spec_tasks());
+                              seq, s, ts));
+    spec_launched = ts.enabled != 0;
   } else {
     HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
     const int npart = row_count_blocks(nrows);
@@ -722,7 +736,13 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, part, s));
     HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, host, seq,
                         s));
-    HIP_TRY(launch_spec_tasks());
+    TaskSpec ts;
+    HIP_TRY(prepare_spec(ts));
+    if (ts.enabled) {
+      HIP_TRY(launch_tasks((const int32_t*)p->row_ptr.ptr, ts.H, ts.nqt_head, ts.ntr, ts.refine_q, 0, ts.order, 0,
+                           ts.parts, ts.slot_base, ts.tasks, dst, s, ts.dev_split, ts.slots, ts.split_tiles));
+      spec_launched = true;
+    }
     // When a column array sized for every block is modest, the compaction is
     // queued before the statistics synchronization, so it overlaps the host's
     // wait and plan selection.

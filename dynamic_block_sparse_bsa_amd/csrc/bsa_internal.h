@@ -135,6 +135,18 @@ hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_h
                                int32_t* seg_ptr, MaskStats* st, hipStream_t s);
 hipError_t launch_mask_compare(const CompareArgs& a, CompareResult* host, unsigned long long seq,
                                hipStream_t s);
+// A task list to build on the device with the split derived from the
+// statistics (k_tasks' device split mode) for an uncoarsened entry: the
+// speculative list of a repeated request key.  enabled = 0: none.
+struct TaskSpec {
+  int32_t enabled;
+  int32_t H, nqt_head, ntr, refine_q, order, dev_split, slots;
+  int32_t* parts;
+  int32_t* slot_base;
+  Task* tasks;
+  int32_t* split_tiles;  // nullable
+};
+
 // Single-launch mask state (counts, statistics, scan, compaction) for masks
 // of at most kSmallMaskBytes bytes, kSmallMaskRows rows and kSmallMaskCols
 // columns at a 16-byte aligned address; outputs as launch_row_count +
@@ -143,8 +155,11 @@ constexpr int kSmallMaskBytes = 32768;
 constexpr int kSmallMaskRows = 2048;
 constexpr int kSmallMaskCols = 256;
 bool mask_small_ok(const uint8_t* mask, int32_t nrows, int32_t nkb);
+// spec.enabled: the kernel also builds that task list, right after the
+// statistics are published and before the compaction.
 hipError_t launch_mask_small(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_ptr, int32_t* cols,
-                             MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s);
+                             MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s,
+                             const TaskSpec& spec);
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
                           int32_t* cols, hipStream_t s);
 hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,

@@ -360,13 +360,22 @@ __device__ inline uint32_t nz_bits16(const u32x4v x) {
 // stored (and published to the host, sequence number last), and only then
 // are the columns compacted from the bitmap, so the host's plan selection
 // overlaps the compaction.  Same outputs as k_row_count + k_scan + k_compact.
+__device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr, int32_t refine_q,
+                            int32_t split, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
+                            int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
+                            int32_t dev_split, int32_t slots, int32_t* __restrict__ split_tiles,
+                            unsigned long long stat_nnz, unsigned stat_max_row);
+
 __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__ mask, int32_t nrows,
                                                      int32_t nkb, int32_t* __restrict__ row_ptr,
                                                      int32_t* __restrict__ cols, MaskStats* st,
-                                                     MaskStats* host_st, unsigned long long seq) {
+                                                     MaskStats* host_st, unsigned long long seq,
+                                                     const TaskSpec spec) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __shared__ uint32_t bits[kSmallMaskBytes / 32 + 1];  // + a zero word read past the last row
-  __shared__ int32_t off[kSmallMaskRows];
+  __shared__ int32_t off[kSmallMaskRows + 1];
+  __shared__ unsigned long long s_nnz;
+  __shared__ unsigned s_maxrow;
   __shared__ int32_t lds[32];
   __shared__ unsigned long long s_long[16];
   __shared__ unsigned s_max[16], s_empty[16];
@@ -463,6 +472,15 @@ __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__
     r.seq = seq;
     *st = r;
     if (host_st) publish_stats(host_st, r);
+    off[nrows] = carry;
+    s_nnz = r.nnz;
+    s_maxrow = r.max_row_nnz;
+  }
+  if (spec.enabled) {
+    // the speculative task list, from the row offsets in LDS
+    __syncthreads();
+    build_tasks(off, spec.H, spec.nqt_head, spec.ntr, spec.refine_q, 0, spec.order, 0, spec.parts,
+                spec.slot_base, spec.tasks, st, spec.dev_split, spec.slots, spec.split_tiles, s_nnz, s_maxrow);
   }
   // column compaction, one thread per row (each row's offset is its own
   // thread's scan result, so no barrier is needed before it)
@@ -608,21 +626,21 @@ __device__ inline Task make_task(const RowTasks& r, int i, int slot0) {
 // dev_split (in halves; 0 = never split) over `slots` resident workgroups
 // and an uncoarsened tile list, so the builder can be queued before the host
 // has read the statistics.
-__global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow_ptr, int32_t H,
-                                                int32_t nqt_head, int32_t ntr, int32_t refine_q,
-                                                int32_t split, int32_t order, int32_t max_len,
-                                                int32_t* __restrict__ parts,
-                                                int32_t* __restrict__ slot_base,
-                                                Task* __restrict__ tasks, MaskStats* st,
-                                                int32_t dev_split, int32_t slots,
-                                                int32_t* __restrict__ split_tiles) {
+// The builder runs in one workgroup of 1024 threads: as its own kernel
+// (k_tasks) or inside k_mask_small.  stat_nnz / stat_max_row are the
+// statistics the device split rule reads (dev_split >= 0).
+__device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr, int32_t refine_q,
+                            int32_t split, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
+                            int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
+                            int32_t dev_split, int32_t slots, int32_t* __restrict__ split_tiles,
+                            unsigned long long stat_nnz, unsigned stat_max_row) {
   __shared__ int32_t lds[32];
   __shared__ int32_t cursor[kLenBuckets];
   const int t = threadIdx.x;
   const int nqt = H * nqt_head;
   if (dev_split >= 0) {
-    const long long W = (long long)refine_q * (long long)st->nnz;
-    const long long row_max = (long long)st->max_row_nnz;
+    const long long W = (long long)refine_q * (long long)stat_nnz;
+    const long long row_max = (long long)stat_max_row;
     long long sp = 0;
     if (dev_split > 0) {
       const long long den = (long long)slots * dev_split;
@@ -733,6 +751,20 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
     carry_s += tot_s;
     __syncthreads();  // this chunk's tasks precede the next chunk's in each bucket
   }
+}
+
+__global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow_ptr, int32_t H,
+                                                int32_t nqt_head, int32_t ntr, int32_t refine_q,
+                                                int32_t split, int32_t order, int32_t max_len,
+                                                int32_t* __restrict__ parts,
+                                                int32_t* __restrict__ slot_base,
+                                                Task* __restrict__ tasks, MaskStats* st,
+                                                int32_t dev_split, int32_t slots,
+                                                int32_t* __restrict__ split_tiles) {
+  const unsigned long long nnz = dev_split >= 0 ? st->nnz : 0ull;
+  const unsigned max_row = dev_split >= 0 ? st->max_row_nnz : 0u;
+  build_tasks(trow_ptr, H, nqt_head, ntr, refine_q, split, order, max_len, parts, slot_base, tasks, st,
+              dev_split, slots, split_tiles, nnz, max_row);
 }
 
 // Stream organization: the concatenated entries of all query tiles (head,
@@ -941,10 +973,11 @@ bool mask_small_ok(const uint8_t* mask, int32_t nrows, int32_t nkb) {
 }
 
 hipError_t launch_mask_small(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_ptr, int32_t* cols,
-                             MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s) {
+                             MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s,
+                             const TaskSpec& spec) {
   if (!mask_small_ok(mask, nrows, nkb)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_mask_small, dim3(1), dim3(1024), 0, s, mask, nrows, nkb, row_ptr, cols, st, host_st,
-                     seq);
+                     seq, spec);
   return hipGetLastError();
 }
 
