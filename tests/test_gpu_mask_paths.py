@@ -33,9 +33,11 @@ def _plan_at(M, block, H, N, offset):
 
 
 # (block, N, H): small masks (single launch when aligned) and large ones with
-# row lengths 625, 469 and 3600 bytes (aligned: 16-byte kernels)
+# row lengths 625, 469 and 3600 bytes, and 2240 rows of 8 bytes (two rows per
+# 16-byte chunk) (aligned: 16-byte kernels)
 @pytest.mark.parametrize("block,N,H", [((64, 64), 1024, 3), ((128, 32), 777, 5), ((32, 128), 5000, 5),
-                                       ((64, 64), 40000, 3), ((32, 128), 60000, 2), ((128, 32), 115200, 1)])
+                                       ((64, 64), 40000, 3), ((32, 128), 60000, 2), ((128, 32), 115200, 1),
+                                       ((32, 128), 1000, 70)])
 def test_mask_paths_agree(block, N, H):
     M, _, _, _ = gen.random_case(H, N, 8, *block, p=0.3, seed=4242 + N, empty_rows={0: [1, 2]},
                                  dense_heads=(H - 1,) if H > 1 else ())
