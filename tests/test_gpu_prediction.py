@@ -81,3 +81,32 @@ def test_table_selection_sequence():
         assert_close(out, oatt.attention(q, k, v, M, *block), f"request {i}")
         prev = info["plan_id"]
         p.destroy()
+
+
+@pytest.mark.parametrize("layout,batch", [("NHD", 2), ("HND", 3)])
+def test_speculative_list_with_batch_and_layout(layout, batch):
+    """Repeats of a batched request in either layout (forced uncoarsened
+    entry, so the key's selection repeats): from the second request on the
+    list is speculative and the outputs match the oracle head by head."""
+    H, N, d, block = 2, 1501, 128, (64, 64)
+    Ht = batch * H
+    pid = next(e["id"] for e in bsa.catalog() if e["name"] == "T64x64_d128_splitk15_lpt")
+    dev = torch.device("cuda")
+    flags = []
+    for i in range(3):
+        M, q, k, v = gen.random_case(Ht, N, d, *block, p=0.25 + 0.1 * i, seed=8300 + 10 * batch + i,
+                                     empty_rows={Ht - 1: [0]})
+        ref = oatt.attention(q, k, v, M, *block)
+        to = (lambda x: x.to(dev).view(batch, H, N, d).permute(0, 2, 1, 3).contiguous()) if layout == "NHD" \
+            else (lambda x: x.to(dev).view(batch, H, N, d).contiguous())
+        qd, kd, vd = to(q), to(k), to(v)
+        Md = torch.from_numpy(np.ascontiguousarray(M)).to(dev).view(batch, H, *M.shape[1:])
+        p = bsa.plan(Md, block, H, N, d, force_plan=pid, batch=batch, layout=layout)
+        out = bsa.run(p, qd, kd, vd)
+        torch.cuda.synchronize()
+        if layout == "NHD":
+            out = out.permute(0, 2, 1, 3)
+        assert_close(out.reshape(Ht, N, d), ref, f"{layout} batch {batch} request {i}")
+        flags.append(p.info["tasks_predicted"])
+        p.destroy()
+    assert flags[1:] == [1, 1]
