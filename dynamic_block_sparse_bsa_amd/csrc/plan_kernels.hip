@@ -482,16 +482,17 @@ __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__
     build_tasks(off, spec.H, spec.nqt_head, spec.ntr, spec.refine_q, 0, spec.order, 0, spec.parts,
                 spec.slot_base, spec.tasks, st, spec.dev_split, spec.slots, spec.split_tiles, s_nnz, s_maxrow);
   }
-  // column compaction, one thread per row (each row's offset is its own
-  // thread's scan result, so no barrier is needed before it)
-  for (int r = t; r < nrows; r += 1024) {
+  // column compaction, one thread per (row, 32-column word): the word's
+  // first output slot is the row offset plus the row's earlier words' bits
+  __syncthreads();
+  for (int it = t; it < nrows * nw; it += 1024) {
+    const int r = it / nw, k = it - r * nw;
     int32_t o = off[r];
-    for (int k = 0; k < nw; ++k) {
-      uint32_t v = row_word(r, k);
-      while (v) {
-        cols[o++] = (k << 5) + __ffs(v) - 1;
-        v &= v - 1u;
-      }
+    for (int kk = 0; kk < k; ++kk) o += (int32_t)__popc(row_word(r, kk));
+    uint32_t v = row_word(r, k);
+    while (v) {
+      cols[o++] = (k << 5) + __ffs(v) - 1;
+      v &= v - 1u;
     }
   }
 }
