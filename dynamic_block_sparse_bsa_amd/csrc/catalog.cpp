@@ -15,7 +15,9 @@ namespace {
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
-constexpr int kXcdRun = 16;  // tasks per XCD run of the "_xcd" organization
+constexpr int kXcdRun = 16;      // tasks per XCD run of the "_xcd" organization
+constexpr int kXcdRunLong = 128; // ... and of "_xcd128" (wan720p-like masks: −2.6%;
+                                 // clustered hunyuan-like masks: +3.5%)
 
 std::vector<CatalogEntry> build_catalog() {
   // kernel tile shapes instantiated for gfx950 (attn_kernels.hip), per head dim
@@ -32,8 +34,10 @@ std::vector<CatalogEntry> build_catalog() {
     // at most 2/split of the even share): split-K balance rule; no split;
     // split-K + runs of kXcdRun consecutive tasks per XCD; longest-first task
     // order without split, with the balance rule, with partitions of half the
-    // balance rule's share, and of two thirds of it
-    const int orgs[][3] = {{2, 0, 0}, {0, 0, 0}, {2, kXcdRun, 0}, {0, 0, 1}, {2, 0, 1}, {4, 0, 1}, {3, 0, 1}};
+    // balance rule's share, and of two thirds of it; split-K + runs of
+    // kXcdRunLong tasks per XCD
+    const int orgs[][3] = {{2, 0, 0},  {0, 0, 0}, {2, kXcdRun, 0}, {0, 0, 1},
+                           {2, 0, 1},  {4, 0, 1}, {3, 0, 1},       {2, kXcdRunLong, 0}};
     for (auto& o : orgs) {
       CatalogEntry e;
       e.id = (int)c.size();
@@ -46,7 +50,7 @@ std::vector<CatalogEntry> build_catalog() {
       char buf[48];
       std::snprintf(buf, sizeof buf, "T%dx%d_d%d_%s%s%s", e.tq, e.tkv, e.d,
                     e.split == 0 ? "nosplit" : e.split == 2 ? "splitk" : e.split == 3 ? "splitk15" : "splitk2",
-                    e.xcd_remap ? "_xcd" : "", e.order ? "_lpt" : "");
+                    e.xcd_remap == kXcdRunLong ? "_xcd128" : e.xcd_remap ? "_xcd" : "", e.order ? "_lpt" : "");
       e.name = buf;
       c.push_back(e);
     }
