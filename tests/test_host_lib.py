@@ -29,7 +29,7 @@ def test_catalog_and_hash():
     shapes = {(e["tile_q"], e["tile_kv"], e["d"]) for e in cat}
     orgs = {(e["split"], e["xcd_remap"], e["order"]) for e in cat}
     assert len(cat) == len(shapes) * len(orgs)  # every organization of every kernel shape
-    assert {(2, 0, 0), (0, 0, 0), (2, 0, 1), (3, 0, 1), (4, 0, 1), (0, 0, 1)} <= orgs
+    assert {(2, 0, 0), (0, 0, 0), (2, 16, 0), (2, 128, 0), (2, 0, 1), (3, 0, 1), (4, 0, 1), (0, 0, 1)} == orgs
     names = [e["name"] for e in cat]
     assert len(set(names)) == len(names)
     assert re.fullmatch(r"[0-9a-f]{16}", bsa.catalog_hash())
