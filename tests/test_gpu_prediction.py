@@ -110,3 +110,36 @@ def test_speculative_list_with_batch_and_layout(layout, batch):
         flags.append(p.info["tasks_predicted"])
         p.destroy()
     assert flags[1:] == [1, 1]
+
+
+def test_speculative_list_for_a_large_mask():
+    """Large mask (the multi-kernel mask state, the speculative builder
+    queued behind the scan): repeats take the speculative list, sampled rows
+    match the oracle, and the task set equals a fresh build's."""
+    H, N, d, block = 4, 20011, 64, (64, 64)
+    pid = next(e["id"] for e in bsa.catalog() if e["name"] == "T64x32_d64_splitk_lpt")
+    rng = np.random.default_rng(8400)
+    dev = torch.device("cuda")
+    flags, sets = [], []
+    for i in range(3):
+        M, q, k, v = gen.random_case(H, N, d, *block, p=0.08 + 0.04 * i, seed=8400 + i)
+        assert M.size > 32768  # not the single-launch mask state
+        p = bsa.plan(torch.from_numpy(np.ascontiguousarray(M)).to(dev), block, H, N, d, force_plan=pid)
+        out = bsa.run(p, q.to(dev), k.to(dev), v.to(dev))
+        torch.cuda.synchronize()
+        rows = {h: np.sort(rng.choice(N, 64, replace=False)) for h in range(H)}
+        ref = oatt.attention_rows(q, k, v, M, *block, rows)
+        o = out.float().cpu().numpy()
+        for h, r in rows.items():
+            assert_close(o[h, r], ref[h], f"request {i} head {h}")
+        flags.append(p.info["tasks_predicted"])
+        if i == 2:
+            sets.append(_task_set(p))
+            fresh = bsa.plan(torch.from_numpy(np.ascontiguousarray(M)).to(dev), block, H, N, d, force_plan=pid,
+                             workspace_limit=1 << 40)
+            assert fresh.info["tasks_predicted"] == 0
+            sets.append(_task_set(fresh))
+            fresh.destroy()
+        p.destroy()
+    assert flags[1:] == [1, 1]
+    assert sets[0] == sets[1]
