@@ -7,11 +7,19 @@ already resident in HBM.  Active-block FLOPs are 4*d*|E(M)|: the per-tile
 accounting of the Tessera paper (section 2.3: QK^T and PV each cost 2*d flops
 per query/key pair) over the effective (query, key) pairs only, clipped at N.
 
-Default workload: the medium request (8 heads, N=8192, d=128, B=(128,128),
-20% i.i.d. + diagonal, one all-active head, one head with two empty
-query-block rows).  --config 1|3|4|5 runs the other workloads.  --config 5 is
-the request stream: each step is the next request of 50 (mask and geometry
-re-drawn per request; one Q/K/V set, whose values do not change the work).
+Default workload: the hunyuan-like layer (24 heads, N=115,200, d=128,
+B=(128,32), clustered top-k mask at 5-30% density per head), the largest
+workload that fits one GPU.  --config 1|2|3|5 runs the others.  --config 5 is
+the request stream: timed step i is request i mod 50 of the stream, in order
+(mask and geometry re-drawn per request; one Q/K/V set, whose values do not
+change the work), so --steps 50 times the whole stream once; the warmup steps
+run requests 0 .. W-1 before it.
+
+CPU baseline: the fp64 oracle as it stands.  For the tiny and medium
+workloads whole heads are timed; for the others a whole head does not fit the
+budget, so seeded random query blocks (every row of each) are timed with the
+oracle's row routine and the active-block flop rate of that sample is
+extrapolated to the request (labelled "extrapolated").
 
 Prints one JSON line.  Single GPU only.
 """
@@ -71,31 +79,76 @@ def load_traffic(workload):
         return None
 
 
-def cpu_baseline(cfg, budget_s):
-    """Time the fp64 oracle, as it stands, on a bounded sample of the workload:
-    whole heads in order (cycling) until the budget is spent."""
-    from oracle import attention as oatt
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    M, BQ, BKV, N, H = cfg["mask"], cfg["BQ"], cfg["BKV"], cfg["N"], cfg["H"]
-    _, per_head = effective_pairs(M, BQ, BKV, N)
+        return os.cpu_count() or 1
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, budget_s, whole_heads):
+    """Time the fp64 oracle, as it stands, on a bounded sample of the workload.
+
+    whole_heads: whole-head evaluations in order (cycling) until the budget is
+    spent.  Otherwise: seeded random query blocks, all rows of each, through
+    the oracle's row routine (it gathers only the active keys), batched per
+    head; the rate of the sample (active-block flops / wall time) is
+    extrapolated to the whole request."""
+    import numpy as np
+    from oracle import attention as oatt
+    cores = _blas_threads()
+    M, BQ, BKV, N, H, d = cfg["mask"], cfg["BQ"], cfg["BKV"], cfg["N"], cfg["H"], cfg["d"]
+    total_pairs, per_head = effective_pairs(M, BQ, BKV, N)
+    Mb = np.asarray(M) != 0
+    ksz = np.minimum(BKV, N - np.arange(Mb.shape[2]) * BKV).astype(np.int64)
     t0 = time.perf_counter()
     n, flops = 0, 0.0
-    while True:
-        h = n % H
-        oatt.attention(cfg["q"][h:h + 1], cfg["k"][h:h + 1], cfg["v"][h:h + 1], M[h:h + 1], BQ, BKV)
-        flops += 4.0 * cfg["d"] * float(per_head[h])
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    if whole_heads:
+        while True:
+            h = n % H
+            oatt.attention(cfg["q"][h:h + 1], cfg["k"][h:h + 1], cfg["v"][h:h + 1], M[h:h + 1], BQ, BKV)
+            flops += 4.0 * d * float(per_head[h])
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        sample = f"fp64 oracle, {n} whole-head evaluations (heads 0..{min(n, H) - 1} of {H}, cycling)"
+    else:
+        rng = np.random.default_rng(12345)
+        nqb = Mb.shape[1]
+        blocks_per_call = 4
+        while True:
+            h = int(rng.integers(H))
+            qbs = rng.choice(nqb, size=min(blocks_per_call, nqb), replace=False)
+            rows = np.concatenate([np.arange(qb * BQ, min(N, (qb + 1) * BQ)) for qb in qbs])
+            oatt.attention_rows(cfg["q"], cfg["k"], cfg["v"], M, BQ, BKV, {h: rows})
+            for qb in qbs:
+                nrow = min(N, (qb + 1) * BQ) - qb * BQ
+                flops += 4.0 * d * nrow * float((Mb[h, qb] * ksz).sum())
+            n += len(qbs)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        sample = (f"fp64 oracle row routine on {n} seeded random query blocks ({n * BQ} rows) of "
+                  f"{H * nqb}; rate extrapolated to the request")
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 oracle, {n} whole-head evaluations (heads 0..{min(n, H) - 1} of {H}, "
-                      f"cycling), all rows, {dt:.1f} s; active-block flops / wall time",
-            "seconds": round(dt, 2)}
+    rate = flops / dt
+    req_flops = 4.0 * d * total_pairs
+    return {"value": float(rate / 1e12), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample}, {dt:.1f} s; active-block flops / wall time",
+            "extrapolated": not whole_heads,
+            "request_s": float(req_flops / rate),
+            "cpu_model": _cpu_model(), "seconds": round(dt, 2)}
 
 
 def main():
@@ -103,7 +156,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--requests", type=int, default=50, help="stream length for --config 5")
     ap.add_argument("--force-plan", type=int, default=-1)
     ap.add_argument("--force-split", type=int, default=-1)
@@ -170,15 +223,17 @@ def main():
     torch.cuda.synchronize()
     req_ms, attn_ms, merge_ms, infos = [], [], [], []
     flops_total = 0.0
+    # timed step i runs request i (mod the stream length): the stream is timed
+    # in order from its first request
     t_start = time.perf_counter()
     for i in range(args.steps):
         t0 = time.perf_counter()
-        a_ms, m_ms, info = request(args.warmup + i, want_info=(i == args.steps - 1))
+        a_ms, m_ms, info = request(i, want_info=(i == args.steps - 1))
         req_ms.append((time.perf_counter() - t0) * 1e3)
         attn_ms.append(a_ms)
         merge_ms.append(m_ms)
         infos.append(info)
-        flops_total += reqs[(args.warmup + i) % len(reqs)][2]
+        flops_total += reqs[i % len(reqs)][2]
     torch.cuda.synchronize()
     total_s = time.perf_counter() - t_start
 
@@ -187,7 +242,7 @@ def main():
     attn_avg = statistics.mean(attn_ms)
     merge_avg = statistics.mean(merge_ms)
     # kernel-side rate: the attention kernel's algorithmic flops / its duration
-    attn_flops = [reqs[(args.warmup + i) % len(reqs)][2] for i in range(args.steps)]
+    attn_flops = [reqs[i % len(reqs)][2] for i in range(args.steps)]
     achieved = sum(attn_flops) / (sum(attn_ms) * 1e-3) / 1e12
     workload = WORKLOAD[args.config]
     info = infos[-1]
@@ -228,10 +283,18 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": load_traffic(workload) if args.layout == "HND" else None},
     }
-    if args.no_cpu or args.config == 5:
+    if args.config == 5:
+        res["stream"] = {"requests_timed": args.steps, "stream_length": len(reqs),
+                         "whole_stream_ms": sum(req_ms[:len(reqs)]) if args.steps >= len(reqs) else None}
+    if args.no_cpu:
         res["cpu_baseline"] = None
     else:
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+        if args.config == 5:
+            BQ0, BKV0, M0, _ = gen.request_c5(0)
+            ccfg = dict(cfg, BQ=BQ0, BKV=BKV0, mask=M0)
+        else:
+            ccfg = cfg
+        res["cpu_baseline"] = cpu_baseline(ccfg, args.cpu_budget, whole_heads=args.config in (1, 2))
     print(json.dumps(res), flush=True)
 
 

@@ -221,7 +221,7 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
     p.groups = (int)std::max<int64_t>(1, std::min<int64_t>(slots, kMaxStreamGroups));
     p.tasks_upper = p.nqt + p.groups;
     p.slots_upper = 2 * (int64_t)p.groups;
-    p.ws_bytes = p.slots_upper * (int64_t)e.tq * (2 * 4 + e.d * 2);
+    p.ws_bytes = p.slots_upper * (int64_t)e.tq * (2 * 4 + e.d * 4);
     return p;
   }
   if (r.force_split > 0) {
@@ -240,7 +240,7 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
     p.slots_upper = 0;
   }
   // per slot and query row: fp32 m and l, then d bf16 partial outputs
-  p.ws_bytes = p.slots_upper * (int64_t)e.tq * (2 * 4 + e.d * 2);
+  p.ws_bytes = p.slots_upper * (int64_t)e.tq * (2 * 4 + e.d * 4);
   return p;
 }
 
@@ -330,8 +330,8 @@ bsa_status validate_request(const bsa_request* rq) {
   const bsa_request fr = folded(*rq);
   const bsa_request* r = &fr;
   if (r->d != 64 && r->d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim %d unsupported (64, 128)", r->d);
-  if (!pow2(r->block_q) || r->block_q < 16 || r->block_q > 256)
-    return fail(BSA_ERR_UNSUPPORTED, "block_q %d unsupported (power of two in [16, 256])", r->block_q);
+  if (!pow2(r->block_q) || r->block_q < 32 || r->block_q > 256)
+    return fail(BSA_ERR_UNSUPPORTED, "block_q %d unsupported (power of two in [32, 256])", r->block_q);
   if (!pow2(r->block_kv) || r->block_kv < 16 || r->block_kv > 256)
     return fail(BSA_ERR_UNSUPPORTED, "block_kv %d unsupported (power of two in [16, 256])", r->block_kv);
   const int64_t nqb = cdiv(r->N, r->block_q), nkb = cdiv(r->N, r->block_kv);
@@ -877,7 +877,7 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   in.max_row_nnz = (int32_t)p->stats.max_row_nnz;
   in.nnz_blocks = (int64_t)p->stats.nnz;
   in.n_tile_rows = (int64_t)r.H * p->ntr;
-  in.n_items = -1;  // known on the device; filled by export
+  in.n_items = -1;  // counts live on the device (the exports return them)
   in.n_tasks = -1;
   in.grid = p->grid;
   in.workspace_bytes = shape.slots_upper > 0 ? shape.ws_bytes : 0;
@@ -925,7 +925,7 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   const int64_t slots = p->shape.slots_upper;
   a.ws_m = ws;
   a.ws_l = ws ? ws + slots * e.tq : nullptr;
-  a.ws_o = ws ? reinterpret_cast<uint32_t*>(ws + 2 * slots * e.tq) : nullptr;
+  a.ws_o = ws ? ws + 2 * slots * e.tq : nullptr;
   // layout: HND = [batch*H][N][d] (one run of heads), NHD = [batch][N][H][d]
   const bool nhd = r.layout == BSA_LAYOUT_NHD;
   a.heads = nhd ? p->heads : r.H;
@@ -1072,8 +1072,6 @@ bsa_status bsa_plan_export_tiles(const bsa_plan* p, int32_t* head, int32_t* q_ti
     }
   }
   *count = n;
-  const_cast<bsa_plan*>(p)->info.n_items = nitems;
-  const_cast<bsa_plan*>(p)->info.n_tasks = (int64_t)nt;
   if (n > cap) return fail(BSA_ERR_INVALID_ARG, "capacity %lld < %lld tiles", (long long)cap, (long long)n);
   return BSA_OK;
 }

@@ -23,9 +23,10 @@
 //    ds_read_b128 and V with the gfx950 transposing read ds_read_b64_tr_b16,
 //    both bank-conflict free.  Tiles are fetched straight into LDS
 //    (global_load_lds) one stage ahead of the tile being computed.
-//  * Softmax runs in the exp2 domain with the 1/sqrt(d) scale folded into one
-//    FMA per score; a fully masked row never produces NaN (running max -inf is
-//    treated as 0 for the exponent offset) and ends with O = 0.
+//  * Softmax runs in the exp2 domain: the exponent of a raw fp32 score s is
+//    fma(s, log2(e)/sqrt(d), -m), one FMA per score, so Q and K enter the
+//    MFMA unmodified; a fully masked row never produces NaN (running max -inf
+//    is treated as 0 for the exponent offset) and ends with O = 0.
 #pragma once
 
 #include <type_traits>
@@ -193,19 +194,16 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
   const int qrow = task.qtile * TQ + w * 32 + n;
 
   // ---- Q fragment: B operand of S^T = K Q^T, resident for the task -------
-  // Q is pre-multiplied by log2(e)/sqrt(d) (and rounded to bf16), so the MFMA
-  // yields scores in log2 units.
+  // Q enters the MFMA exactly as given (bf16): the scale log2(e)/sqrt(d) is
+  // applied to the fp32 scores, so it adds no rounding of its own.  Rows past
+  // N read row 0 (finite values, never written back).
   bf16x8 qf[S::DK];
   {
-    const bool ok = qrow < N;
-    const __bf16* qp = a.q + head_off + (size_t)(ok ? qrow : 0) * RS + 8 * hh;
+    const __bf16* qp = a.q + head_off + (size_t)(qrow < N ? qrow : 0) * RS + 8 * hh;
 #pragma unroll
-    for (int c = 0; c < S::DK; ++c) {
-      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)(ok ? (float)raw[e] * a.scale_log2 : 0.0f);
-    }
+    for (int c = 0; c < S::DK; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
   }
+  const float scale = a.scale_log2;
 
   // membership: which logical sub-row of a coarsened tile this wave covers
   const int sub_row = (a.coarsen_q > 1) ? (w * 32) / a.bq : 0;
@@ -213,16 +211,15 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
   const uint32_t full_kv_all = 0xffffffffu;  // uncoarsened tiles: every block active
 
   // ---- online-softmax state (lane-local; l is a half-sum over this lane's keys)
-  // m_run is a reference maximum in log2 units; it is raised only when a score
-  // exceeds it by more than 8, so P stays <= 2^8 and the O rescale is rare.
-  // The QK^T accumulator starts from cm = -m_run (0 while m_run = -inf), so
-  // the MFMA emits exponents ready for v_exp_f32: no per-score subtract.
+  // m_run is a reference maximum in log2 units; it is raised only when a
+  // scaled score exceeds it by more than 8, so P stays <= 2^8 and the O
+  // rescale is rare.  The exponent of a raw score s is fma(s, scale, negm)
+  // with negm = -m_run (0 while m_run = -inf, so a masked score stays -inf).
   float m_run = -INFINITY;
+  float negm = 0.0f;
   float l_run = 0.0f;
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
-  f32x16 cm;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) cm[v] = 0.0f;
+  const f32x16 zero16 = {};
   f32x16 acc[S::DB];
 #pragma unroll
   for (int b = 0; b < S::DB; ++b) acc[b] = f32x16{};
@@ -407,7 +404,7 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
           constexpr int later = (NK - 1 - i) < (KPF - 1) ? (NK - 1 - i) : (KPF - 1);
           lgkm_wait<later>(kr[i % KPF]);
           const bf16x8 kf = __builtin_bit_cast(bf16x8, kr[i % KPF]);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? cm : s[st], 0, 0, 0);
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], c == 0 ? zero16 : s[st], 0, 0, 0);
           if constexpr (i + KPF < NK) kread(std::integral_constant<int, i + KPF>{});
         });
       }
@@ -432,37 +429,32 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
             if (st * 32 + 16 * (v >> 3) + (v & 7) >= lim) s[st][v] = -INFINITY;
       }
       // ---- online softmax (exp2 domain, lazy rescale) ---------------------
-      // Scores are s - m_use; the reference is raised when one exceeds it by
-      // more than 8 (or at the row's first active key).
+      // The row maximum is taken on the raw scores (the scale is positive)
+      // and converted to log2 units; the reference is raised when it exceeds
+      // m_run by more than 8 (or at the row's first active key).
       float mx = -INFINITY;
 #pragma unroll
       for (int st = 0; st < S::NST; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
-      mx = fmaxf(mx, other_half(mx));
+      mx = fmaxf(mx, other_half(mx)) * scale;
       const bool first = (m_run == -INFINITY) && (mx != -INFINITY);
-      const bool grow = first || (mx > 8.0f);
+      const bool grow = first || (mx > m_run + 8.0f);
       if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float delta = grow ? mx : 0.0f;
-        const float alpha = (grow && !first) ? __builtin_amdgcn_exp2f(-delta) : 1.0f;
-        if (grow) m_run = (first ? 0.0f : m_run) + delta;
+        const float alpha = (grow && !first) ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+        if (grow) m_run = mx;
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < S::DB; ++b) acc[b] *= alpha;
-#pragma unroll
-        for (int st = 0; st < S::NST; ++st)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) s[st][v] -= delta;
-        const float neg = (m_run == -INFINITY) ? 0.0f : -m_run;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) cm[v] = neg;
+        negm = (m_run == -INFINITY) ? 0.0f : -m_run;
       }
 
       bf16x8 pf[S::NST][2];
 #pragma unroll
       for (int st = 0; st < S::NST; ++st)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) pf[st][v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(s[st][v]);
+        for (int v = 0; v < 16; ++v)
+          pf[st][v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[st][v], scale, negm));
       // l accumulates the bf16-rounded probabilities that enter the PV
       // product, two per v_dot2 against (1, 1).
 #pragma unroll
@@ -560,17 +552,16 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
       a.ws_m[sl * TQ + r] = m_run;
       a.ws_l[sl * TQ + r] = l_tot;
     }
-    // the partial output normalized by its own l, as bf16 pairs (d, d+1) so
+    // the partial output normalized by its own l, fp32, [d][T_Q] per slot:
     // each lane stores 4 bytes and a wave's 32 rows fill 128 contiguous bytes
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    uint32_t* wo = a.ws_o + sl * (size_t)(D / 2) * TQ;
+    float* wo = a.ws_o + sl * (size_t)D * TQ;
 #pragma unroll
     for (int b = 0; b < S::DB; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const int dd = b * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);  // even
-        const bf16x2 pr = {(__bf16)(acc[b][v] * inv), (__bf16)(acc[b][v + 1] * inv)};
-        wo[(size_t)(dd >> 1) * TQ + r] = __builtin_bit_cast(uint32_t, pr);
+      for (int v = 0; v < 16; ++v) {
+        const int dd = b * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        wo[(size_t)dd * TQ + r] = acc[b][v] * inv;
       }
   }
 #endif

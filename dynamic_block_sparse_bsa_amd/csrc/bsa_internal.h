@@ -73,8 +73,8 @@ struct AttnArgs {
   const uint32_t* tbits;  // membership bits per tile-list entry, or nullptr
   float* ws_m;            // [slot][T_Q]           running max (log2 units)
   float* ws_l;            // [slot][T_Q]           exponential sum
-  uint32_t* ws_o;         // [slot][d/2][T_Q] bf16 pairs (d, d+1): the partial
-                          // output normalized by its own l (0 when l = 0)
+  float* ws_o;            // [slot][d][T_Q] fp32: the partial output
+                          // normalized by its own l (0 when l = 0)
   // Tensor layout (elements; d is contiguous): head g of the task list is
   // head g % heads of batch entry g / heads, at g/heads * batch_stride +
   // g%heads * head_stride, and consecutive rows are row_stride apart.
@@ -106,7 +106,7 @@ struct MergeArgs {
   const int32_t* slot_base; // [n_qtiles] first workspace slot of the query tile
   const float* ws_m;
   const float* ws_l;
-  const uint32_t* ws_o;     // [slot][d/2][T_Q] bf16 pairs, normalized partials
+  const float* ws_o;        // [slot][d][T_Q] fp32, normalized partials
   // Optional compact list of the split query tiles (ascending) and its
   // device count; the launch then loops over (listed tile, column group)
   // items instead of one workgroup per (tile, column group).

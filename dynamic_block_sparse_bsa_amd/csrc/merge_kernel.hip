@@ -9,8 +9,9 @@
 // owns one row (t mod T_Q) and 4-column quads of it; it computes its row's
 // weights w_p l_p / sum_q w_q l_q in registers (each partial is its
 // partition's output normalized by its own exponential sum, so the weights
-// carry l_p) and streams the partial outputs, stored as [slot][d/2][T_Q] bf16
-// pairs, with the loads of all partitions in flight together (addresses past
+// carry l_p) and streams the partial outputs, stored as [slot][d][T_Q] fp32
+// (so a split row is rounded to bf16 once, at the output, like an unsplit
+// one), with the loads of all partitions in flight together (addresses past
 // the last partition are clamped to it and weighted 0).  No LDS and no
 // barrier.  HBM-bound: each partial element is read once and each output
 // element written once.
@@ -70,22 +71,18 @@ __device__ __forceinline__ void merge_row(const MergeRow& m, int q0, int qstep) 
   row_weights<P>(m, w);
   for (int qi = q0; qi < kCols / 4; qi += qstep) {
     const int c = m.c0 + qi * 4;
-    uint32_t x0[P], x1[P];
+    float x[P][4];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const uint32_t* o = a.ws_o + (size_t)(m.sb + min(p, m.parts - 1)) * (a.d / 2) * m.TQ +
-                          (size_t)(c >> 1) * m.TQ + m.r;
-      x0[p] = o[0];      // columns (c, c+1)
-      x1[p] = o[m.TQ];   // columns (c+2, c+3)
+      const float* o = a.ws_o + (size_t)(m.sb + min(p, m.parts - 1)) * a.d * m.TQ + (size_t)c * m.TQ + m.r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[p][i] = o[(size_t)i * m.TQ];  // column c + i
     }
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      acc[0] += w[p] * __uint_as_float(x0[p] << 16);
-      acc[1] += w[p] * __uint_as_float(x0[p] & 0xffff0000u);
-      acc[2] += w[p] * __uint_as_float(x1[p] << 16);
-      acc[3] += w[p] * __uint_as_float(x1[p] & 0xffff0000u);
-    }
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += w[p] * x[p][i];
     store_quad(m, c, acc);
   }
 }
@@ -113,12 +110,9 @@ __device__ void merge_row_any(const MergeRow& m, int q0, int qstep) {
       const size_t s = (size_t)(m.sb + p) * m.TQ + m.r;
       const float l = a.ws_l[s];
       const float w = l > 0.0f ? __builtin_amdgcn_exp2f(a.ws_m[s] - mstar) * l * inv : 0.0f;
-      const uint32_t* o = a.ws_o + (size_t)(m.sb + p) * (a.d / 2) * m.TQ + (size_t)(c >> 1) * m.TQ + m.r;
-      const uint32_t x0 = o[0], x1 = o[m.TQ];
-      acc[0] += w * __uint_as_float(x0 << 16);
-      acc[1] += w * __uint_as_float(x0 & 0xffff0000u);
-      acc[2] += w * __uint_as_float(x1 << 16);
-      acc[3] += w * __uint_as_float(x1 & 0xffff0000u);
+      const float* o = a.ws_o + (size_t)(m.sb + p) * a.d * m.TQ + (size_t)c * m.TQ + m.r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += w * o[(size_t)i * m.TQ];
     }
     store_quad(m, c, acc);
   }

@@ -100,8 +100,10 @@ typedef struct {
   int32_t max_row_nnz;  /* largest active-block count of a query-block row      */
   int64_t nnz_blocks;   /* active logical blocks                                */
   int64_t n_tile_rows;  /* rows of the tile list (query tiles or tile rows)     */
-  int64_t n_items;      /* entries of the tile list                             */
-  int64_t n_tasks;      /* workgroup tasks of the attention launch              */
+  int64_t n_items;      /* -1: the tile-list length lives on the device
+                           (bsa_plan_export_tiles returns the tile count)       */
+  int64_t n_tasks;      /* -1: the task count lives on the device
+                           (bsa_plan_export_tasks returns it)                   */
   int64_t grid;         /* workgroups launched (>= n_tasks)                     */
   int64_t workspace_bytes; /* split-K workspace bound to the plan               */
   int64_t long_run_blocks; /* active blocks inside runs of length >= 2          */

@@ -50,3 +50,36 @@ def tile_cells(p, block, N):
             assert ok.all(), "membership bit set outside the mask grid"
             np.add.at(cov, (head[sel], r, c), 1)
     return cov, cq, ckv
+
+
+def cell_counts_by_head(p, block, N):
+    """Per head h, the multiplicity with which the plan's exported tiles cover
+    each cell of min(B_Q, T_Q) x min(B_KV, T_KV) tokens: yields (h, counts
+    [nq, nk] int64).  Tiles are grouped by head first, so memory stays at one
+    head's cell grid at full workload sizes."""
+    info = p.info
+    TQ, TKV = info["tile_q"], info["tile_kv"]
+    cQ, cKV = info["coarsen_q"], info["coarsen_kv"]
+    BQ, BKV = block
+    cq, ckv = min(BQ, TQ), min(BKV, TKV)
+    nq, nk = -(-N // cq), -(-N // ckv)
+    head, qt, kt, bits = p.export_tiles()
+    order = np.argsort(head, kind="stable")
+    head, qt, kt, bits = head[order], qt[order], kt[order], bits[order]
+    bounds = np.searchsorted(head, np.arange(p.H + 1))
+    assert bounds[-1] == head.size, "tile with a head index out of range"
+    for h in range(p.H):
+        s, e = bounds[h], bounds[h + 1]
+        q_h = qt[s:e].astype(np.int64)
+        k_h = kt[s:e].astype(np.int64)
+        b_h = bits[s:e]
+        cnt = np.zeros(nq * nk, dtype=np.int64)
+        for a in range(cQ):
+            for b in range(cKV):
+                sel = ((b_h >> np.uint32(a * cKV + b)) & 1).astype(bool)
+                r = q_h[sel] * cQ + a
+                c = k_h[sel] * cKV + b
+                assert ((r >= 0) & (r < nq) & (c >= 0) & (c < nk)).all(), \
+                    "membership bit set outside the mask grid"
+                cnt += np.bincount(r * nk + c, minlength=nq * nk)
+        yield h, cnt.reshape(nq, nk)

@@ -166,6 +166,13 @@ def test_layout_and_batch_validation():
     # NHD rows of one head are H*d elements apart: N * H * d * 2 bytes must stay below 2^31
     assert _create_status(H=64, N=131072, layout="NHD") == "BSA_ERR_UNSUPPORTED"
     assert _create_status(mask_ptr=None, layout="NHD") == "BSA_ERR_INVALID_ARG"
+    # block geometries outside the documented ranges are refused before any
+    # launch (the mask pointer is never read)
+    assert _create_status(block=(16, 64)) == "BSA_ERR_UNSUPPORTED"
+    assert _create_status(block=(512, 64)) == "BSA_ERR_UNSUPPORTED"
+    assert _create_status(block=(64, 8)) == "BSA_ERR_UNSUPPORTED"
+    assert _create_status(block=(48, 64)) == "BSA_ERR_UNSUPPORTED"
+    assert _create_status(d=96) == "BSA_ERR_UNSUPPORTED"
     with pytest.raises(bsa.BsaError):
         bsa.tensor_shapes(4, 1024, 128, layout="HDN")
 

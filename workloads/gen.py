@@ -139,16 +139,19 @@ def mask_clustered(H, N, BQ, BKV, seed, rho=(0.05, 0.30), nclusters=16, rank=8,
     return M
 
 
-def qkv(H, N, d, seeds, threads=8):
-    """bf16 CPU tensors Q, K, V [H, N, d]; element ~ N(0,1) float32 then RNE."""
+def qkv(H, N, d, seeds, threads=8, std=(1.0, 1.0, 1.0)):
+    """bf16 CPU tensors Q, K, V [H, N, d]; element ~ N(0, std^2) float32 then
+    RNE (std per tensor; the default is the workloads' N(0, 1))."""
     import torch
 
     out = []
-    for s in seeds:
+    for s, sd in zip(seeds, std):
         t = torch.empty((H, N, d), dtype=torch.bfloat16)
 
-        def fill(h, s=s, t=t):
+        def fill(h, s=s, t=t, sd=sd):
             a = _rng(s, h).standard_normal((N, d), dtype=np.float32)
+            if sd != 1.0:
+                a *= np.float32(sd)
             t[h] = torch.from_numpy(a).to(torch.bfloat16)
 
         with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -198,10 +201,10 @@ def config(c, r=0, with_qkv=True):
     return cfg
 
 
-def random_case(H, N, d, BQ, BKV, p, seed, empty_rows=None, dense_heads=()):
+def random_case(H, N, d, BQ, BKV, p, seed, empty_rows=None, dense_heads=(), std=(1.0, 1.0, 1.0)):
     """Small test case: i.i.d. mask plus diagonal, Q/K/V from the same seeds."""
     M = mask_iid_diag(H, N, BQ, BKV, p, seed, dense_heads=dense_heads, empty_rows=empty_rows)
-    q, k, v = qkv(H, N, d, (seed + 1, seed + 2, seed + 3))
+    q, k, v = qkv(H, N, d, (seed + 1, seed + 2, seed + 3), std=std)
     return M, q, k, v
 
 
