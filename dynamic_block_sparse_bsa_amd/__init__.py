@@ -91,6 +91,7 @@ def _load():
     L.bsa_plan_cache_get.argtypes = [P, ctypes.POINTER(Request), P, ctypes.POINTER(P), ctypes.POINTER(i32)]
     L.bsa_plan_cache_destroy.argtypes = [P]
     L.bsa_plan_cache_run.argtypes = [P, ctypes.POINTER(Request), P, P, P, P, P, ctypes.POINTER(i32)]
+    L.bsa_attention_noalloc.argtypes = [ctypes.POINTER(Request), P, P, P, P, P]
     for f in ("bsa_table_version", "bsa_catalog_hash", "bsa_status_string", "bsa_last_error"):
         getattr(L, f).restype = ctypes.c_char_p
     L.bsa_status_string.argtypes = [i32]
@@ -99,7 +100,7 @@ def _load():
               "bsa_plan_export_tasks",
               "bsa_catalog_get", "bsa_plan_eligible", "bsa_select", "bsa_table_load",
               "bsa_base_plan", "bsa_plan_cache_create", "bsa_plan_cache_get", "bsa_plan_cache_destroy",
-              "bsa_plan_cache_run"):
+              "bsa_plan_cache_run", "bsa_attention_noalloc"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -306,6 +307,21 @@ def run(p, q, k, v, out=None, stream=None):
     out = _tensors(p, q, k, v, out)
     _check(_load().bsa_run(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            _stream(stream)))
+    return out
+
+
+def attention_noalloc(mask, block, H, N, d, q, k, v, out, force_plan=-1, force_split=-1, workspace_limit=0,
+                      stream=None, batch=1, layout="HND"):
+    """bsa_attention_noalloc: O = BSA(Q, K, V) for the request in one call,
+    every device buffer carved from the library's fixed per-device scratch
+    (no device allocation; `out` must be given).  Returns out."""
+    import types
+    req = _mask_request(mask, block, H, N, d, force_plan, force_split, workspace_limit, batch, layout)
+    if out is None:
+        raise BsaError("BSA_ERR_INVALID_ARG", "out must be given (this entry point allocates nothing)")
+    out = _tensors(types.SimpleNamespace(H=H, N=N, d=d, batch=batch, layout=layout), q, k, v, out)
+    _check(_load().bsa_attention_noalloc(ctypes.byref(req), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         out.data_ptr(), _stream(stream)))
     return out
 
 

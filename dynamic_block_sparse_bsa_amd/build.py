@@ -27,7 +27,8 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(HERE, "..", "include"),
 ]
-SOURCES = ["api.cpp", "catalog.cpp", "plan_kernels.hip", "merge_kernel.hip", "attn_kernels.hip"]
+SOURCES = ["api.cpp", "catalog.cpp", "plan_kernels.hip", "merge_kernel.hip", "attn_kernels.hip",
+           "static_scratch.hip"]
 # MFMA accumulators in VGPRs: the softmax reads every score, and AGPR operands
 # would need a v_accvgpr_read per element.
 EXTRA = {"attn_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -82,6 +82,7 @@ struct DevBuf {
   void* ptr = nullptr;
   size_t cap = 0;
   int dev = -1;
+  bool pooled = false;  // from the cache (returned to it on release)
 };
 
 hipError_t pool_alloc(int dev, size_t bytes, DevBuf* b) {
@@ -95,6 +96,7 @@ hipError_t pool_alloc(int dev, size_t bytes, DevBuf* b) {
       g_pool.idle -= cap;
       b->cap = cap;
       b->dev = dev;
+      b->pooled = true;
       return hipSuccess;
     }
   }
@@ -102,11 +104,16 @@ hipError_t pool_alloc(int dev, size_t bytes, DevBuf* b) {
   if (e != hipSuccess) return e;
   b->cap = cap;
   b->dev = dev;
+  b->pooled = true;
   return hipSuccess;
 }
 
 void pool_release(DevBuf* b) {
   if (!b->ptr) return;
+  if (!b->pooled) {  // carved from the static scratch: nothing to return
+    b->ptr = nullptr;
+    return;
+  }
   std::lock_guard<std::mutex> lk(g_pool.mu);
   if (g_pool.idle + b->cap > Pool::kIdleCap) {
     (void)hipFree(b->ptr);
@@ -116,6 +123,31 @@ void pool_release(DevBuf* b) {
   }
   b->ptr = nullptr;
 }
+
+// Bump allocator over the library's fixed per-device scratch array, for the
+// entry point that allocates nothing: buffers are carved 256-byte aligned and
+// are never returned one by one (the next call starts over).
+struct Arena {
+  char* base = nullptr;
+  size_t cap = 0;
+  size_t used = 0;
+  size_t left() const { return cap - std::min(cap, (used + 255) & ~size_t(255)); }
+};
+
+hipError_t arena_alloc(Arena* a, int dev, size_t bytes, DevBuf* b) {
+  const size_t off = (a->used + 255) & ~size_t(255);
+  const size_t n = bytes ? bytes : 1;
+  if (off > a->cap || n > a->cap - off) return hipErrorOutOfMemory;
+  b->ptr = a->base + off;
+  b->cap = n;
+  b->dev = dev;
+  b->pooled = false;
+  a->used = off + n;
+  return hipSuccess;
+}
+
+// 256-byte aligned size of a buffer carved from the arena
+size_t arena_size(size_t bytes) { return ((bytes ? bytes : 1) + 255) & ~size_t(255); }
 
 constexpr size_t kEarlyCompactBytes = size_t(16) << 20;
 
@@ -239,7 +271,7 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
     p.tasks_upper = p.nqt;
     p.slots_upper = 0;
   }
-  // per slot and query row: fp32 m and l, then d bf16 partial outputs
+  // per slot and query row: fp32 m and l, then d fp32 partial outputs
   p.ws_bytes = p.slots_upper * (int64_t)e.tq * (2 * 4 + e.d * 4);
   return p;
 }
@@ -273,6 +305,7 @@ void event_put(int dev, bool timing, hipEvent_t e) {
 }  // namespace
 
 struct bsa_plan {
+  Arena* arena = nullptr;  // non-null: every buffer comes from the static scratch
   bsa_request req{};    // batch folded into H (req.H = batch * heads, req.batch = 1)
   int32_t heads = 0;    // heads per batch entry, as requested
   int dev = 0;
@@ -292,6 +325,10 @@ struct bsa_plan {
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};  // timing events of bsa_run_timed
   hipEvent_t done = nullptr;  // recorded after plan creation and after untimed runs
   hipEvent_t last = nullptr;  // recorded after the plan's latest stream work (done or ev[2])
+
+  hipError_t alloc(size_t bytes, DevBuf* b) {
+    return arena ? arena_alloc(arena, dev, bytes, b) : pool_alloc(dev, bytes, b);
+  }
 
   ~bsa_plan() {
     for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &row_part, &cols, &trow_cnt, &trow_ptr_buf, &tcol_buf,
@@ -641,24 +678,52 @@ bsa_status bsa_base_plan(const bsa_request* req, int32_t* plan_id) {
   return BSA_OK;
 }
 
-bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out) {
-  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
-  *out = nullptr;
+// Device bytes a candidate plan adds to the shared mask state when its
+// buffers are carved from the arena (tile list of a coarsened mapping, task
+// list, split bookkeeping, split-K workspace), each rounded as the arena does.
+static size_t plan_bytes(const CatalogEntry& e, const bsa_request& r, const PlanShape& sh, const MaskStats& st,
+                         int nqb, int nkb) {
+  (void)e;
+  (void)nkb;
+  const size_t nnz = std::max<size_t>((size_t)st.nnz, 1);
+  const size_t nqt = (size_t)sh.nqt;
+  size_t b = 0;
+  if (sh.mq.coarsen > 1 || sh.mk.coarsen > 1) {
+    const size_t ntrows = (size_t)r.H * (size_t)cdiv(nqb, sh.mq.coarsen);
+    b += arena_size(sizeof(int32_t) * ntrows) + arena_size(sizeof(int32_t) * (ntrows + 1)) +
+         arena_size(sizeof(int32_t) * nnz) + arena_size(sizeof(uint32_t) * nnz);
+  }
+  b += 2 * arena_size(sizeof(int32_t) * nqt) + arena_size(sizeof(Task) * (size_t)std::max<int64_t>(sh.tasks_upper, 1));
+  if (sh.groups > 0) b += arena_size(sizeof(int32_t) * (size_t)(sh.groups + 1));
+  else if (sh.split > 0) b += arena_size(sizeof(int32_t) * nqt);
+  if (sh.slots_upper > 0) b += arena_size((size_t)sh.ws_bytes);
+  return b;
+}
+
+// Plan creation.  arena == nullptr: buffers from the device memory cache,
+// statistics through the thread's coherent host record.  Otherwise every
+// buffer is carved from the arena (the static scratch), the statistics come
+// back by one stream-ordered copy, no task list is built speculatively, and
+// candidate plans whose buffers do not fit the arena's remaining space are
+// ineligible (the workspace condition of section 4.4).
+static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::unique_ptr<bsa_plan>& p,
+                                   Arena* arena) {
   bsa_status vs = validate_request(req);
   if (vs != BSA_OK) return vs;
   const int32_t heads = req->H;
   const bsa_request fr = folded(*req);
   req = &fr;
-  hipStream_t s = (hipStream_t)stream;
-  std::unique_ptr<bsa_plan> p(new bsa_plan());
+  p.reset(new bsa_plan());
+  p->arena = arena;
   p->heads = heads;
   // On an error return, kernels already queued may still use the plan's
   // buffers: wait for the stream before they go back to the cache.
   struct DrainOnError {
     std::unique_ptr<bsa_plan>& plan;
     hipStream_t stream;
+    bool ok = false;
     ~DrainOnError() {
-      if (plan) (void)hipStreamSynchronize(stream);
+      if (plan && !ok) (void)hipStreamSynchronize(stream);
     }
   } drain{p, s};
   p->req = *req;
@@ -670,14 +735,28 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   const int nrows = r.H * p->nqb;
 
   // ---- shared mask state: counts, offsets, columns, statistics ---------------
-  MaskStats* host = pinned_stats();
-  if (!host) return fail(BSA_ERR_NO_MEMORY, "pinned host allocation failed");
-  HIP_TRY(pool_alloc(p->dev, sizeof(MaskStats), &p->stats_dev));
-  HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)nrows + 1), &p->row_ptr));
+  MaskStats* host = nullptr;
+  if (arena) {
+    // the mask state's own buffers must fit before anything is launched
+    const size_t need = arena_size(sizeof(MaskStats)) + arena_size(sizeof(int32_t) * ((size_t)nrows + 1)) +
+                        (mask_small_ok(r.mask, nrows, p->nkb)
+                             ? arena_size(sizeof(int32_t) * (size_t)nrows * (size_t)p->nkb)
+                             : arena_size(sizeof(int32_t) * (size_t)nrows) +
+                                   arena_size(sizeof(RowPartial) * (size_t)row_count_blocks(nrows)));
+    if (need > arena->left())
+      return fail(BSA_ERR_UNSUPPORTED, "request needs %zu bytes of mask state, the static scratch holds %zu",
+                  need, arena->cap);
+  } else {
+    host = pinned_stats();
+    if (!host) return fail(BSA_ERR_NO_MEMORY, "pinned host allocation failed");
+  }
+  HIP_TRY(p->alloc(sizeof(MaskStats), &p->stats_dev));
+  HIP_TRY(p->alloc(sizeof(int32_t) * ((size_t)nrows + 1), &p->row_ptr));
   MaskStats* dst = (MaskStats*)p->stats_dev.ptr;
   // speculative task list of the entry this request key selected last time
+  // (not with the static scratch: its space goes to the selected plan)
   const PredKey pkey = pred_key(p->dev, r);
-  const int pred_id = pred_lookup(pkey);
+  const int pred_id = arena ? -1 : pred_lookup(pkey);
   bool spec_launched = false;
   // Allocates the speculative buffers and fills `ts` (ts.enabled stays 0
   // when there is no usable prediction).
@@ -694,11 +773,11 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     // W / split <= slots * split share / 2 for the balance rule
     const int64_t cap = nqt + (dev_split > 0 ? slots * dev_split / 2 + 2 : 0);
     hipError_t err;
-    if ((err = pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->spec_parts)) != hipSuccess) return err;
-    if ((err = pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->spec_slot)) != hipSuccess) return err;
-    if ((err = pool_alloc(p->dev, sizeof(Task) * (size_t)std::max<int64_t>(cap, 1), &p->spec_tasks)) != hipSuccess)
+    if ((err = p->alloc(sizeof(int32_t) * (size_t)nqt, &p->spec_parts)) != hipSuccess) return err;
+    if ((err = p->alloc(sizeof(int32_t) * (size_t)nqt, &p->spec_slot)) != hipSuccess) return err;
+    if ((err = p->alloc(sizeof(Task) * (size_t)std::max<int64_t>(cap, 1), &p->spec_tasks)) != hipSuccess)
       return err;
-    if (dev_split > 0 && (err = pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->spec_split)) != hipSuccess)
+    if (dev_split > 0 && (err = p->alloc(sizeof(int32_t) * (size_t)nqt, &p->spec_split)) != hipSuccess)
       return err;
     ts.enabled = 1;
     ts.H = r.H;
@@ -721,7 +800,7 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   if (mask_small_ok(r.mask, nrows, p->nkb)) {
     // small mask: counts, statistics, scan and compaction in one launch
     early_compact = true;
-    HIP_TRY(pool_alloc(p->dev, cols_bound, &p->cols));
+    HIP_TRY(p->alloc(cols_bound, &p->cols));
     // (with a prediction, the same kernel also builds the speculative list)
     TaskSpec ts;
     HIP_TRY(prepare_spec(ts));
@@ -729,9 +808,9 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
                               seq, s, ts));
     spec_launched = ts.enabled != 0;
   } else {
-    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
+    HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
     const int npart = row_count_blocks(nrows);
-    HIP_TRY(pool_alloc(p->dev, sizeof(RowPartial) * (size_t)npart, &p->row_part));
+    HIP_TRY(p->alloc(sizeof(RowPartial) * (size_t)npart, &p->row_part));
     RowPartial* part = (RowPartial*)p->row_part.ptr;
     HIP_TRY(launch_row_count(r.mask, nrows, p->nkb, (int32_t*)p->row_cnt.ptr, part, s));
     HIP_TRY(launch_scan((int32_t*)p->row_cnt.ptr, (int32_t*)p->row_ptr.ptr, nrows, part, npart, dst, host, seq,
@@ -745,20 +824,25 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     }
     // When a column array sized for every block is modest, the compaction is
     // queued before the statistics synchronization, so it overlaps the host's
-    // wait and plan selection.
-    early_compact = cols_bound <= kEarlyCompactBytes;
+    // wait and plan selection (not with the static scratch, whose space is
+    // sized by the exact count instead).
+    early_compact = !arena && cols_bound <= kEarlyCompactBytes;
     if (early_compact) {
-      HIP_TRY(pool_alloc(p->dev, cols_bound, &p->cols));
+      HIP_TRY(p->alloc(cols_bound, &p->cols));
       HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
     }
   }
   // Wait for the statistics alone (the compaction may still run): spin on the
-  // sequence number the scan kernel stores last.
-  {
+  // sequence number the scan kernel stores last.  With the static scratch:
+  // one stream-ordered copy of the device record and a stream synchronization.
+  if (host) {
     const bsa_status ws = wait_host_seq(&host->seq, seq, s, "mask statistics");
     if (ws != BSA_OK) return ws;
+    std::memcpy(&p->stats, host, sizeof(MaskStats));
+  } else {
+    HIP_TRY(hipMemcpyAsync(&p->stats, dst, sizeof(MaskStats), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
   }
-  std::memcpy(&p->stats, host, sizeof(MaskStats));
   const double total_blocks = (double)r.H * p->nqb * p->nkb;
   const double density = p->stats.nnz / total_blocks;
   const double runcov = p->stats.nnz ? (double)p->stats.long_run / (double)p->stats.nnz : 0.0;
@@ -776,10 +860,22 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   const CatalogEntry* chosen = nullptr;
   PlanShape shape;
   std::string why = "no candidate";
+  // with the static scratch: the bytes left once the block-CSR columns
+  // (compacted after the statistics) are carved
+  const size_t nnz_cols =
+      early_compact ? 0 : arena_size(sizeof(int32_t) * std::max<size_t>((size_t)p->stats.nnz, 1));
+  const size_t arena_left = arena ? (arena->left() > nnz_cols ? arena->left() - nnz_cols : 0) : 0;
+  if (arena && arena->left() < nnz_cols)
+    return fail(BSA_ERR_UNSUPPORTED, "request needs %zu bytes of block-CSR columns, %zu of the %zu-byte static "
+                "scratch are left", nnz_cols, arena->left(), arena->cap);
   for (int c : sel.candidates) {
     const CatalogEntry& e = catalog()[c];
     if (!attn_launcher(e.tq, e.tkv, e.d)) continue;
     PlanShape sh = shape_plan(e, r, p->stats, p->dev);
+    if (arena && plan_bytes(e, r, sh, p->stats, p->nqb, p->nkb) > arena_left) {
+      why = "buffers exceed the static scratch";
+      continue;
+    }
     if (eligible(e, r, sh.ws_bytes, &why)) {
       chosen = &e;
       shape = sh;
@@ -796,7 +892,7 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   // ---- block-CSR columns (unless queued before the synchronization) ----------
   const size_t nnz = (size_t)p->stats.nnz;
   if (!early_compact) {
-    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->cols));
+    HIP_TRY(p->alloc(sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->cols));
     HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
   }
 
@@ -807,10 +903,10 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     p->ntr = (int)cdiv(p->nqb, cq);
     const int ntc = (int)cdiv(p->nkb, ckv);
     const int ntrows = r.H * p->ntr;
-    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)ntrows, &p->trow_cnt));
-    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * ((size_t)ntrows + 1), &p->trow_ptr_buf));
-    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->tcol_buf));
-    HIP_TRY(pool_alloc(p->dev, sizeof(uint32_t) * std::max<size_t>(nnz, 1), &p->tbits_buf));
+    HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)ntrows, &p->trow_cnt));
+    HIP_TRY(p->alloc(sizeof(int32_t) * ((size_t)ntrows + 1), &p->trow_ptr_buf));
+    HIP_TRY(p->alloc(sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->tcol_buf));
+    HIP_TRY(p->alloc(sizeof(uint32_t) * std::max<size_t>(nnz, 1), &p->tbits_buf));
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
                            ntc, (int32_t*)p->trow_cnt.ptr, nullptr, nullptr, nullptr, s));
     HIP_TRY(launch_scan((int32_t*)p->trow_cnt.ptr, (int32_t*)p->trow_ptr_buf.ptr, ntrows, nullptr, 0, nullptr,
@@ -832,15 +928,15 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   const int64_t nqt = shape.nqt;
   const bool spec_hit = spec_launched && chosen->id == pred_id && shape.groups == 0;
   if (!spec_hit) {
-    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->parts));
-    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->slot_off));
-    HIP_TRY(pool_alloc(p->dev, sizeof(Task) * (size_t)std::max<int64_t>(shape.tasks_upper, 1), &p->tasks));
+    HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)nqt, &p->parts));
+    HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)nqt, &p->slot_off));
+    HIP_TRY(p->alloc(sizeof(Task) * (size_t)std::max<int64_t>(shape.tasks_upper, 1), &p->tasks));
   }
   const int64_t max_len = shape.split > 0 ? shape.split
                                           : std::min<int64_t>((int64_t)shape.mq.coarsen * p->stats.max_row_nnz,
                                                               1 << 30);
   if (shape.groups > 0) {
-    HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)(shape.groups + 1), &p->seg_ptr));
+    HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)(shape.groups + 1), &p->seg_ptr));
     HIP_TRY(launch_tasks_stream(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.groups,
                                 (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr, (Task*)p->tasks.ptr,
                                 (int32_t*)p->seg_ptr.ptr, dst, s));
@@ -852,13 +948,13 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
     std::swap(p->tasks, p->spec_tasks);
     std::swap(p->split_tiles, p->spec_split);
   } else {
-    if (shape.split > 0) HIP_TRY(pool_alloc(p->dev, sizeof(int32_t) * (size_t)nqt, &p->split_tiles));
+    if (shape.split > 0) HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)nqt, &p->split_tiles));
     HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split, chosen->order,
                          (int32_t)max_len, (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr,
                          (Task*)p->tasks.ptr, dst, s, -1, 0, (int32_t*)p->split_tiles.ptr));
   }
-  pred_store(pkey, predictable(*chosen, r) && shape.groups == 0 ? chosen->id : -1);
-  if (shape.slots_upper > 0) HIP_TRY(pool_alloc(p->dev, (size_t)shape.ws_bytes, &p->ws));
+  if (!arena) pred_store(pkey, predictable(*chosen, r) && shape.groups == 0 ? chosen->id : -1);
+  if (shape.slots_upper > 0) HIP_TRY(p->alloc((size_t)shape.ws_bytes, &p->ws));
   const int64_t gran = chosen->xcd_remap > 0 && shape.groups == 0 ? 8 * (int64_t)chosen->xcd_remap : 1;
   p->grid = shape.groups > 0 ? shape.groups : cdiv(std::max<int64_t>(shape.tasks_upper, 1), gran) * gran;
   if (p->grid >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many tasks");
@@ -887,10 +983,36 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
   in.row_skew = skew;
   in.host_select_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
   in.tasks_predicted = spec_hit ? 1 : 0;
-  HIP_TRY(event_get(p->dev, false, &p->done));
-  HIP_TRY(hipEventRecord(p->done, s));
-  p->last = p->done;
+  if (!arena) {
+    HIP_TRY(event_get(p->dev, false, &p->done));
+    HIP_TRY(hipEventRecord(p->done, s));
+    p->last = p->done;
+  }
+  drain.ok = true;
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  std::unique_ptr<bsa_plan> p;
+  const bsa_status st = plan_create_impl(req, (hipStream_t)stream, p, nullptr);
+  if (st != BSA_OK) return st;
   *out = p.release();
+  return BSA_OK;
+}
+
+// Tensor arguments of a run for a request with its batch folded into H:
+// non-null, 16-byte aligned, O disjoint from Q, K and V.
+static bsa_status check_tensors(const bsa_request& r, const void* q, const void* k, const void* v, const void* o) {
+  if (!q || !k || !v || !o) return fail(BSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  for (const void* ptr : {q, k, v, o})
+    if (((uintptr_t)ptr) & 15) return fail(BSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const uintptr_t bytes = (uintptr_t)r.H * r.N * r.d * 2;
+  for (const void* in : {q, k, v}) {
+    const uintptr_t a = (uintptr_t)in, b = (uintptr_t)o;
+    if (a < b + bytes && b < a + bytes) return fail(BSA_ERR_INVALID_ARG, "O overlaps Q, K or V");
+  }
   return BSA_OK;
 }
 
@@ -900,14 +1022,10 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
                            hipStream_t s, bool timed, float* attn_ms, float* merge_ms,
                            const unsigned long long* guard) {
   if (!p) return fail(BSA_ERR_INVALID_ARG, "plan is NULL");
-  if (!q || !k || !v || !o) return fail(BSA_ERR_INVALID_ARG, "NULL tensor pointer");
-  for (const void* ptr : {q, k, v, (const void*)o})
-    if (((uintptr_t)ptr) & 15) return fail(BSA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   const bsa_request& r = p->req;
-  const uintptr_t bytes = (uintptr_t)r.H * r.N * r.d * 2;
-  for (const void* in : {q, k, v}) {
-    const uintptr_t a = (uintptr_t)in, b = (uintptr_t)o;
-    if (a < b + bytes && b < a + bytes) return fail(BSA_ERR_INVALID_ARG, "O overlaps Q, K or V");
+  {
+    const bsa_status cs = check_tensors(r, q, k, v, o);
+    if (cs != BSA_OK) return cs;
   }
   const CatalogEntry& e = *p->entry;
   AttnLauncher fn = attn_launcher(e.tq, e.tkv, e.d);
@@ -977,7 +1095,7 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
     }
     HIP_TRY(launch_merge(m, (int32_t)p->shape.nqt, s, grid_items));
   }
-  if (!timed) {
+  if (!timed && mp->done) {
     HIP_TRY(hipEventRecord(mp->done, s));
     mp->last = mp->done;
   }
@@ -1001,6 +1119,31 @@ bsa_status bsa_run(const bsa_plan* p, const void* q, const void* k, const void* 
 bsa_status bsa_run_timed(const bsa_plan* p, const void* q, const void* k, const void* v, void* o, void* stream,
                          float* attn_ms, float* merge_ms) {
   return run_impl(p, q, k, v, o, (hipStream_t)stream, true, attn_ms, merge_ms, nullptr);
+}
+
+bsa_status bsa_attention_noalloc(const bsa_request* req, const void* q, const void* k, const void* v, void* o,
+                                 void* stream) {
+  {
+    const bsa_status vs = validate_request(req);
+    if (vs != BSA_OK) return vs;
+    const bsa_status cs = check_tensors(folded(*req), q, k, v, o);
+    if (cs != BSA_OK) return cs;
+  }
+  void* base = nullptr;
+  size_t cap = 0;
+  HIP_TRY(static_scratch(&base, &cap));
+  // the last 64 KiB of the array are never carved: a guard band between
+  // the final buffer and the end of the array
+  Arena arena;
+  arena.base = (char*)base;
+  arena.cap = cap - (size_t(64) << 10);
+  hipStream_t s = (hipStream_t)stream;
+  std::unique_ptr<bsa_plan> p;
+  const bsa_status st = plan_create_impl(req, s, p, &arena);
+  if (st != BSA_OK) return st;
+  // the plan's buffers stay in the scratch (nothing is returned to a cache),
+  // so the kernels queued here may outlive the host-side plan record
+  return run_impl(p.get(), q, k, v, o, s, false, nullptr, nullptr, nullptr);
 }
 
 bsa_status bsa_plan_destroy(bsa_plan* p) {

@@ -182,6 +182,12 @@ hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, in
 constexpr int kMergeCols = 16;
 hipError_t launch_merge(const MergeArgs& a, int32_t n_qtiles, hipStream_t s, int32_t grid_items = 0);
 
+// Fixed per-device scratch array of the entry point that allocates nothing
+// (static_scratch.hip): its device address on the current device (looked up
+// once per device) and its size in bytes.
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 // Attention kernel table: returns nullptr when (tq, tkv, d) has no kernel.
 AttnLauncher attn_launcher(int tq, int tkv, int d);
 // Resident workgroups per CU of that kernel (0 if it has none).

@@ -150,6 +150,29 @@ bsa_status bsa_run(const bsa_plan* plan, const void* q, const void* k, const voi
 bsa_status bsa_run_timed(const bsa_plan* plan, const void* q, const void* k, const void* v,
                          void* o, void* stream, float* attn_ms, float* merge_ms);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: O = BSA(Q, K,
+ * V) for `req` in one call, the same computation as bsa_plan_create +
+ * bsa_run + bsa_plan_destroy, with tensors as for bsa_run, but every device
+ * buffer of the request (mask state, tile and task lists, split-K workspace)
+ * is carved from a fixed scratch array of 128 MiB per device that the
+ * library holds until the process ends.  No hipMalloc, hipFree or pinned
+ * host allocation is made (the array's address is looked up once per
+ * device).  Plans whose buffers do not fit the space left after the mask
+ * state are not eligible, so the ranked selection may pick a different plan
+ * than bsa_plan_create; no task list is built speculatively.
+ * Synchronizes `stream` once (for the mask statistics) and returns once O's
+ * kernels are queued.  Every call on one GPU uses that GPU's one scratch
+ * array, which keeps the last call's contents: calls that overlap on one GPU
+ * (on different streams or threads) race and must be ordered by the caller;
+ * calls on one stream are ordered by it.  Errors: those of bsa_plan_create
+ * and bsa_run, checked before any launch; BSA_ERR_UNSUPPORTED with the sizes
+ * in bsa_last_error() when the request's mask state, or every eligible
+ * plan, needs more than the scratch (the block-CSR size is known only after
+ * the mask-state kernels have run; O is then left untouched). */
+bsa_status bsa_attention_noalloc(const bsa_request* req, const void* q, const void* k, const void* v,
+                                 void* o, void* stream);
+
 /* Release a plan.  Waits for the plan's latest stream work (its creation or
  * its most recent run) first; runs must not be in flight on other streams.
  * NULL is accepted. */
