@@ -211,10 +211,10 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
   const uint32_t full_kv_all = 0xffffffffu;  // uncoarsened tiles: every block active
 
   // ---- online-softmax state (lane-local; l is a half-sum over this lane's keys)
-  // m_run is a reference maximum in log2 units; it is raised only when a
-  // scaled score exceeds it by more than 8, so P stays <= 2^8 and the O
-  // rescale is rare.  The exponent of a raw score s is fma(s, scale, negm)
-  // with negm = -m_run (0 while m_run = -inf, so a masked score stays -inf).
+  // m_run is the row's reference in log2 units: the maximum of the tile that
+  // last moved it (see the softmax step).  The exponent of a raw score s is
+  // fma(s, scale, negm) with negm = -m_run (0 while m_run = -inf, so a
+  // masked score stays -inf).
   float m_run = -INFINITY;
   float negm = 0.0f;
   float l_run = 0.0f;
@@ -428,44 +428,61 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
           for (int v = 0; v < 16; ++v)
             if (st * 32 + 16 * (v >> 3) + (v & 7) >= lim) s[st][v] = -INFINITY;
       }
-      // ---- online softmax (exp2 domain, lazy rescale) ---------------------
-      // The row maximum is taken on the raw scores (the scale is positive)
-      // and converted to log2 units; the reference is raised when it exceeds
-      // m_run by more than 8 (or at the row's first active key).
-      float mx = -INFINITY;
+      // ---- online softmax (exp2 domain, optimistic reference) -------------
+      // Each score's exponent is fma(s, scale, -m_run) against the row's
+      // reference m_run (log2 units).  The reference moves only when it must:
+      // at the row's first active tile (no reference yet), or when this
+      // tile's weights sum to more than 2^64 (a score about 59 or more above
+      // the reference, or an exp overflow to infinity).  Then the tile's row
+      // maximum becomes the reference, O and l are rescaled and the tile's
+      // weights are recomputed.  Weights up to 2^64 lose nothing in bf16 P or
+      // the fp32 sums, so the row maximum -- eight dependent v_max3, a lane
+      // exchange and the compares -- is skipped on almost every tile.  l sums
+      // the bf16-rounded weights that enter the PV product, two per v_dot2
+      // against (1, 1), in two independent chains.
+      bf16x8 pf[S::NST][2];
+      float lt0 = 0.0f, lt1 = 0.0f;
+      auto weights = [&]() {
 #pragma unroll
-      for (int st = 0; st < S::NST; ++st)
+        for (int st = 0; st < S::NST; ++st)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
-      mx = fmaxf(mx, other_half(mx)) * scale;
-      const bool first = (m_run == -INFINITY) && (mx != -INFINITY);
-      const bool grow = first || (mx > m_run + 8.0f);
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = (grow && !first) ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+          for (int v = 0; v < 16; ++v)
+            pf[st][v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[st][v], scale, negm));
+        lt0 = 0.0f;
+        lt1 = 0.0f;
+#pragma unroll
+        for (int st = 0; st < S::NST; ++st)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 p0 = {pf[st][0][2 * e], pf[st][0][2 * e + 1]};
+            const bf16x2 p1 = {pf[st][1][2 * e], pf[st][1][2 * e + 1]};
+            lt0 = __builtin_amdgcn_fdot2_f32_bf16(p0, ones2, lt0, false);
+            lt1 = __builtin_amdgcn_fdot2_f32_bf16(p1, ones2, lt1, false);
+          }
+      };
+      bool redo = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0ull;
+      if (!redo) {
+        weights();
+        redo = __builtin_amdgcn_ballot_w64(!(lt0 + lt1 <= 0x1p64f)) != 0ull;
+      }
+      if (redo) {
+        // the row maximum is taken on the raw scores (the scale is positive)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < S::NST; ++st)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
+        mx = fmaxf(mx, other_half(mx)) * scale;
+        const bool grow = mx > m_run;  // also at the first tile (m_run = -inf)
+        const float alpha = (grow && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
         if (grow) m_run = mx;
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < S::DB; ++b) acc[b] *= alpha;
         negm = (m_run == -INFINITY) ? 0.0f : -m_run;
+        weights();
       }
-
-      bf16x8 pf[S::NST][2];
-#pragma unroll
-      for (int st = 0; st < S::NST; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          pf[st][v >> 3][v & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[st][v], scale, negm));
-      // l accumulates the bf16-rounded probabilities that enter the PV
-      // product, two per v_dot2 against (1, 1).
-#pragma unroll
-      for (int st = 0; st < S::NST; ++st)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bf16x2 pp = {pf[st][h2][2 * e], pf[st][h2][2 * e + 1]};
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run, false);
-          }
+      l_run += lt0 + lt1;
       // ---- O^T += V^T P^T; V^T fragments via LDS transpose reads ----------
       // The product runs in chunks of (one 32-wide d-block) x (up to two
       // 32-key sub-tiles); the reads of chunk q+1 are in flight while the
