@@ -3,7 +3,7 @@
     python -m dynamic_block_sparse_bsa_amd.build  [--jobs N]
 
 Every translation unit is compiled with hipcc for gfx950 only.  The built-in
-plan table (tables/gfx950_v1.txt) is embedded into the library as a string.
+plan table (tables/gfx950_v2.txt) is embedded into the library as a string.
 """
 
 import argparse
@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
-TABLE = os.path.join(HERE, "tables", "gfx950_v1.txt")
+TABLE = os.path.join(HERE, "tables", "gfx950_v2.txt")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

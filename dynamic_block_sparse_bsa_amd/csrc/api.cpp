@@ -239,7 +239,7 @@ struct PlanShape {
 
 PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStats& st, int dev) {
   PlanShape p;
-  p.mq = map_dim(r.block_q, e.tq, 32);
+  p.mq = map_dim(r.block_q, e.tq, kMinCoarsenBlockQ);
   p.mk = map_dim(r.block_kv, e.tkv, 1);
   p.nqt_head = (int)cdiv(r.N, e.tq);
   p.nqt = (int64_t)r.H * p.nqt_head;
@@ -367,8 +367,8 @@ bsa_status validate_request(const bsa_request* rq) {
   const bsa_request fr = folded(*rq);
   const bsa_request* r = &fr;
   if (r->d != 64 && r->d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim %d unsupported (64, 128)", r->d);
-  if (!pow2(r->block_q) || r->block_q < 32 || r->block_q > 256)
-    return fail(BSA_ERR_UNSUPPORTED, "block_q %d unsupported (power of two in [32, 256])", r->block_q);
+  if (!pow2(r->block_q) || r->block_q < 16 || r->block_q > 256)
+    return fail(BSA_ERR_UNSUPPORTED, "block_q %d unsupported (power of two in [16, 256])", r->block_q);
   if (!pow2(r->block_kv) || r->block_kv < 16 || r->block_kv > 256)
     return fail(BSA_ERR_UNSUPPORTED, "block_kv %d unsupported (power of two in [16, 256])", r->block_kv);
   const int64_t nqb = cdiv(r->N, r->block_q), nkb = cdiv(r->N, r->block_kv);
@@ -568,7 +568,7 @@ PredKey pred_key(int dev, const bsa_request& r) {
 // by k_tasks with the plan's own split rule or none.
 bool predictable(const CatalogEntry& e, const bsa_request& r) {
   if (r.force_split != -1 && r.force_split != 0) return false;
-  const DimMap mq = map_dim(r.block_q, e.tq, 32), mk = map_dim(r.block_kv, e.tkv, 1);
+  const DimMap mq = map_dim(r.block_q, e.tq, kMinCoarsenBlockQ), mk = map_dim(r.block_kv, e.tkv, 1);
   return mq.ok && mk.ok && mq.coarsen == 1 && mk.coarsen == 1;
 }
 
@@ -765,7 +765,7 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
     if (pred_id < 0 || pred_id >= (int)catalog().size()) return hipSuccess;
     const CatalogEntry& e = catalog()[pred_id];
     if (!predictable(e, r) || !attn_launcher(e.tq, e.tkv, e.d)) return hipSuccess;
-    const DimMap mq = map_dim(r.block_q, e.tq, 32);
+    const DimMap mq = map_dim(r.block_q, e.tq, kMinCoarsenBlockQ);
     const int nqt_head = (int)cdiv(r.N, e.tq);
     const int64_t nqt = (int64_t)r.H * nqt_head;
     const int dev_split = r.force_split == 0 ? 0 : e.split;

@@ -206,8 +206,16 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
   const float scale = a.scale_log2;
 
   // membership: which logical sub-row of a coarsened tile this wave covers
-  const int sub_row = (a.coarsen_q > 1) ? (w * 32) / a.bq : 0;
+  // Membership of a coarsened tile: bit a*coarsen_kv + b marks logical block
+  // (a, b) of the tile active.  With B_Q >= 32 all 32 rows of a wave lie in
+  // one logical row, sub_row; with B_Q = 16 they span rows 2w and 2w + 1
+  // (lane n's row is 2w + n/16), so the skip test uses both rows' bits and
+  // the masking is per lane.
+  const bool lane_rows = a.bq < 32;
+  const int sub_row = (a.coarsen_q > 1) ? (lane_rows ? 2 * w : (w * 32) / a.bq) : 0;
   const uint32_t full_kv = (a.coarsen_kv >= 32) ? 0xffffffffu : ((1u << a.coarsen_kv) - 1u);
+  const uint32_t wave_kv = lane_rows ? (full_kv | (full_kv << a.coarsen_kv)) : full_kv;
+  const int lane_shift = lane_rows ? (n >> 4) * a.coarsen_kv : 0;
   const uint32_t full_kv_all = 0xffffffffu;  // uncoarsened tiles: every block active
 
   // ---- online-softmax state (lane-local; l is a half-sum over this lane's keys)
@@ -364,7 +372,7 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
   auto step = [&](auto stage_c) {
     constexpr int buf = decltype(stage_c)::value;
     const int cur_kv0 = kvq[0];
-    const uint32_t wbits = (bitsq[0] >> (sub_row * a.coarsen_kv)) & full_kv;
+    const uint32_t wbits = (bitsq[0] >> (sub_row * a.coarsen_kv)) & wave_kv;
     const int jn = j + NSTAGE - 1;
     int kvn = N;
     uint32_t bitsn = 0u;
@@ -410,13 +418,25 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
       }
       // ---- masking: inactive logical blocks of the tile, keys >= N ---------
       // A 16-key group (st, v/8) never straddles a logical K/V block (B_KV >=
-      // 16), so membership is one wave-uniform bit test per group.
-      if (wbits != full_kv) {
+      // 16), so membership is one bit test per group: wave-uniform, or per
+      // lane when the wave's rows span two logical rows.
+      if (wbits != wave_kv) {
+        if (!lane_rows) {
 #pragma unroll
-        for (int g = 0; g < 2 * S::NST; ++g) {
-          if (!((wbits >> ((16 * g) >> a.bkv_log2)) & 1u)) {
+          for (int g = 0; g < 2 * S::NST; ++g) {
+            if (!((wbits >> ((16 * g) >> a.bkv_log2)) & 1u)) {
 #pragma unroll
-            for (int v = 0; v < 8; ++v) s[g >> 1][8 * (g & 1) + v] = -INFINITY;
+              for (int v = 0; v < 8; ++v) s[g >> 1][8 * (g & 1) + v] = -INFINITY;
+            }
+          }
+        } else {
+          const uint32_t lbits = (wbits >> lane_shift) & full_kv;
+#pragma unroll
+          for (int g = 0; g < 2 * S::NST; ++g) {
+            const bool off = !((lbits >> ((16 * g) >> a.bkv_log2)) & 1u);
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+              s[g >> 1][8 * (g & 1) + v] = off ? -INFINITY : s[g >> 1][8 * (g & 1) + v];
           }
         }
       }

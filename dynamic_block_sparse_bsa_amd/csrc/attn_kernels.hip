@@ -7,19 +7,15 @@ namespace bsa {
 AttnLauncher attn_launcher(int tq, int tkv, int d) {
 #define BSA_CASE(TQ_, TKV_, D_) \
   if (tq == TQ_ && tkv == TKV_ && d == D_) return &launch_attn<TQ_, TKV_, D_>;
-  BSA_CASE(64, 32, 128)
   BSA_CASE(64, 64, 128)
   BSA_CASE(128, 32, 128)
   BSA_CASE(128, 64, 128)
   BSA_CASE(128, 128, 128)
-  BSA_CASE(256, 32, 128)
   BSA_CASE(256, 64, 128)
   BSA_CASE(64, 32, 64)
   BSA_CASE(64, 64, 64)
   BSA_CASE(128, 32, 64)
   BSA_CASE(128, 64, 64)
-  BSA_CASE(128, 128, 64)
-  BSA_CASE(256, 64, 64)
 #undef BSA_CASE
   return nullptr;
 }
@@ -44,19 +40,15 @@ static int wg_per_cu(bool stream) {
 int attn_wg_per_cu(int tq, int tkv, int d, bool stream) {
 #define BSA_CASE(TQ_, TKV_, D_) \
   if (tq == TQ_ && tkv == TKV_ && d == D_) return wg_per_cu<TQ_, TKV_, D_>(stream);
-  BSA_CASE(64, 32, 128)
   BSA_CASE(64, 64, 128)
   BSA_CASE(128, 32, 128)
   BSA_CASE(128, 64, 128)
   BSA_CASE(128, 128, 128)
-  BSA_CASE(256, 32, 128)
   BSA_CASE(256, 64, 128)
   BSA_CASE(64, 32, 64)
   BSA_CASE(64, 64, 64)
   BSA_CASE(128, 32, 64)
   BSA_CASE(128, 64, 64)
-  BSA_CASE(128, 128, 64)
-  BSA_CASE(256, 64, 64)
 #undef BSA_CASE
   return 0;
 }

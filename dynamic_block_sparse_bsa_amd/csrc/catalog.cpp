@@ -19,38 +19,56 @@ constexpr int kXcdRun = 16;      // tasks per XCD run of the "_xcd" organization
 constexpr int kXcdRunLong = 128; // ... and of "_xcd128" (wan720p-like masks: −2.6%;
                                  // clustered hunyuan-like masks: +3.5%)
 
+// Task organizations {split, XCD runs, order} (split in halves: partitions
+// of at most 2/split of the even share of entries per resident workgroup
+// slot; order 1 = longest task first).
+struct Org {
+  const char* name;
+  int split, xcd, order;
+};
+constexpr Org kSplitK = {"splitk", 2, 0, 0};  // the default (base) organization
+constexpr Org kSplitKLpt = {"splitk_lpt", 2, 0, 1};
+constexpr Org kNoSplitLpt = {"nosplit_lpt", 0, 0, 1};
+constexpr Org kSplitKXcd = {"splitk_xcd", 2, kXcdRun, 0};
+constexpr Org kSplitK15Lpt = {"splitk15_lpt", 3, 0, 1};
+constexpr Org kSplitK2Lpt = {"splitk2_lpt", 4, 0, 1};
+constexpr Org kSplitKXcd128 = {"splitk_xcd128", 2, kXcdRunLong, 0};
+
 std::vector<CatalogEntry> build_catalog() {
-  // kernel tile shapes instantiated for gfx950 (attn_kernels.hip), per head dim
+  // Kernel tile shapes instantiated for gfx950 (attn_kernels.hip) and the
+  // organizations offered with each.  Every shape has the default
+  // organization (a key's base plan uses it); the others were kept where
+  // they were the fastest plan on some profiling cases: of 104 shape x
+  // organization entries, dropping all but these 31 raised the corpus's
+  // best-achievable geometric-mean latency by under 0.1%.
   struct Shape {
     int tq, tkv, d;
+    std::vector<Org> orgs;
   };
-  static const Shape shapes[] = {{64, 32, 128},  {64, 64, 128},  {128, 32, 128}, {128, 64, 128},
-                                 {128, 128, 128}, {256, 32, 128}, {256, 64, 128}, {64, 32, 64},
-                                 {64, 64, 64},   {128, 32, 64},  {128, 64, 64},  {128, 128, 64},
-                                 {256, 64, 64}};
+  const std::vector<Shape> shapes = {
+      {128, 32, 128, {kSplitK, kSplitKLpt, kNoSplitLpt, kSplitKXcd, kSplitK15Lpt, kSplitK2Lpt, kSplitKXcd128}},
+      {128, 64, 128, {kSplitK, kSplitKLpt, kNoSplitLpt, kSplitKXcd, kSplitK15Lpt, kSplitK2Lpt, kSplitKXcd128}},
+      {64, 64, 128, {kSplitK, kSplitKXcd}},
+      {256, 64, 128, {kSplitK, kSplitKXcd, kSplitK15Lpt}},
+      {128, 128, 128, {kSplitK}},
+      {64, 64, 64, {kSplitK}},
+      {64, 32, 64, {kSplitK, kNoSplitLpt, kSplitKXcd128}},
+      {128, 32, 64, {kSplitK, kNoSplitLpt}},
+      {128, 64, 64, {kSplitK, kNoSplitLpt, kSplitKLpt, kSplitK2Lpt, kSplitKXcd}},
+  };
   std::vector<CatalogEntry> c;
-  for (const Shape& s : shapes) {
-    // organizations {split, XCD runs, order} (split in halves: partitions of
-    // at most 2/split of the even share): split-K balance rule; no split;
-    // split-K + runs of kXcdRun consecutive tasks per XCD; longest-first task
-    // order without split, with the balance rule, with partitions of half the
-    // balance rule's share, and of two thirds of it; split-K + runs of
-    // kXcdRunLong tasks per XCD
-    const int orgs[][3] = {{2, 0, 0},  {0, 0, 0}, {2, kXcdRun, 0}, {0, 0, 1},
-                           {2, 0, 1},  {4, 0, 1}, {3, 0, 1},       {2, kXcdRunLong, 0}};
-    for (auto& o : orgs) {
+  for (const Shape& sh : shapes) {
+    for (const Org& o : sh.orgs) {
       CatalogEntry e;
       e.id = (int)c.size();
-      e.tq = s.tq;
-      e.tkv = s.tkv;
-      e.d = s.d;
-      e.split = o[0];
-      e.xcd_remap = o[1];
-      e.order = o[2];
+      e.tq = sh.tq;
+      e.tkv = sh.tkv;
+      e.d = sh.d;
+      e.split = o.split;
+      e.xcd_remap = o.xcd;
+      e.order = o.order;
       char buf[48];
-      std::snprintf(buf, sizeof buf, "T%dx%d_d%d_%s%s%s", e.tq, e.tkv, e.d,
-                    e.split == 0 ? "nosplit" : e.split == 2 ? "splitk" : e.split == 3 ? "splitk15" : "splitk2",
-                    e.xcd_remap == kXcdRunLong ? "_xcd128" : e.xcd_remap ? "_xcd" : "", e.order ? "_lpt" : "");
+      std::snprintf(buf, sizeof buf, "T%dx%d_d%d_%s", e.tq, e.tkv, e.d, o.name);
       e.name = buf;
       c.push_back(e);
     }
@@ -153,8 +171,9 @@ bool eligible(const CatalogEntry& e, const bsa_request& r, int64_t ws_bytes, std
   if (r.dtype != BSA_DTYPE_BF16) return no("dtype");
   if (r.layout != BSA_LAYOUT_HND && r.layout != BSA_LAYOUT_NHD) return no("layout");
   if (r.d != e.d) return no("head dim");
-  // a wave owns 32 query rows, so a coarsened query tile needs B_Q >= 32
-  DimMap mq = map_dim(r.block_q, e.tq, 32);
+  // a wave owns 32 query rows: a coarsened query tile needs B_Q >= 16 (with
+  // B_Q = 16 the kernel resolves a wave's two logical rows per lane)
+  DimMap mq = map_dim(r.block_q, e.tq, kMinCoarsenBlockQ);
   DimMap mk = map_dim(r.block_kv, e.tkv, 1);
   if (!mq.ok) return no("query geometry");
   if (!mk.ok) return no("key/value geometry");

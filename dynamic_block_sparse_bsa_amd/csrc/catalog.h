@@ -38,6 +38,9 @@ struct DimMap {
   int refine = 1;   // tiles per logical block
 };
 
+// Smallest logical query block a coarsened query tile may hold: a wave owns
+// 32 query rows, which then span at most two logical rows.
+constexpr int kMinCoarsenBlockQ = 16;
 DimMap map_dim(int block, int tile, int min_coarsen_block);
 
 const std::vector<CatalogEntry>& catalog();

@@ -502,8 +502,11 @@ __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__
 // [tc*ckv, tc*ckv + ckv).  A tile exists iff one of its blocks is active;
 // its membership bit a*ckv + b is set iff logical block
 // (tr*cq + a, tc*ckv + b) is active (paper section 4.2, "Coarsened").
-// One workgroup per tile row; the row's union is built in an LDS bitmap.
-// With trow_ptr == nullptr the kernel writes counts, else the tile entries.
+// One workgroup per tile row; the row's union is built in an LDS bitmap of
+// kCoarsenWin tile columns, one window of columns after another (a single
+// window unless the row has more than kCoarsenWin tile columns).  With
+// trow_ptr == nullptr the kernel writes counts, else the tile entries.
+constexpr int kCoarsenWin = 8192;
 __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row_ptr,
                                                  const int32_t* __restrict__ cols, int32_t nqb,
                                                  int32_t cq, int32_t ckv, int32_t ntr,
@@ -511,55 +514,61 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
                                                  const int32_t* __restrict__ trow_ptr,
                                                  int32_t* __restrict__ tcol,
                                                  uint32_t* __restrict__ tbits) {
-  extern __shared__ uint32_t bitmap[];
+  __shared__ uint32_t bitmap[kCoarsenWin];
   __shared__ int32_t wave_tot[4];
   const int g = blockIdx.x;  // h * ntr + tr
   const int h = g / ntr;
   const int tr = g - h * ntr;
-  for (int i = threadIdx.x; i < ntc; i += 256) bitmap[i] = 0u;
-  __syncthreads();
-  for (int a = 0; a < cq; ++a) {
-    const int r = tr * cq + a;
-    if (r >= nqb) break;
-    const int rr = h * nqb + r;
-    const int b = row_ptr[rr], e = row_ptr[rr + 1];
-    for (int i = b + threadIdx.x; i < e; i += 256) {
-      const int c = cols[i];
-      const int tc = c / ckv;
-      atomicOr(&bitmap[tc], 1u << (a * ckv + (c - tc * ckv)));
-    }
-  }
-  __syncthreads();
   const unsigned l = lane_id();
   const int w = threadIdx.x >> 6;
+  int cnt = 0;                                   // count pass: this thread's share
+  int32_t out = trow_ptr ? trow_ptr[g] : 0;      // write pass: next entry
+  for (int w0 = 0; w0 < ntc; w0 += kCoarsenWin) {
+    const int wn = min(kCoarsenWin, ntc - w0);
+    for (int i = threadIdx.x; i < wn; i += 256) bitmap[i] = 0u;
+    __syncthreads();
+    for (int a = 0; a < cq; ++a) {
+      const int r = tr * cq + a;
+      if (r >= nqb) break;
+      const int rr = h * nqb + r;
+      const int b = row_ptr[rr], e = row_ptr[rr + 1];
+      for (int i = b + threadIdx.x; i < e; i += 256) {
+        const int c = cols[i];
+        const int tc = c / ckv - w0;
+        if (tc >= 0 && tc < wn) atomicOr(&bitmap[tc], 1u << (a * ckv + (c - (tc + w0) * ckv)));
+      }
+    }
+    __syncthreads();
+    if (!trow_ptr) {
+      for (int i = threadIdx.x; i < wn; i += 256) cnt += bitmap[i] != 0u;
+    } else {
+      // ordered compaction: process the window in chunks of 256 entries
+      for (int base = 0; base < wn; base += 256) {
+        const int i = base + threadIdx.x;
+        const uint32_t bits = i < wn ? bitmap[i] : 0u;
+        const unsigned long long bal = __ballot(bits != 0u);
+        if (l == 0) wave_tot[w] = __popcll(bal);
+        __syncthreads();
+        int before = 0;
+        for (int k = 0; k < w; ++k) before += wave_tot[k];
+        const int total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+        if (bits) {
+          const int pos = out + before + (int)prefix_count(bal);
+          tcol[pos] = w0 + i;
+          tbits[pos] = bits;
+        }
+        out += total;
+        __syncthreads();
+      }
+    }
+    __syncthreads();  // the window is read out before the next one is cleared
+  }
   if (!trow_ptr) {
-    int cnt = 0;
-    for (int i = threadIdx.x; i < ntc; i += 256) cnt += bitmap[i] != 0u;
     // wave reduction then workgroup reduction
     for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
     if (l == 0) wave_tot[w] = cnt;
     __syncthreads();
     if (threadIdx.x == 0) trow_cnt[g] = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-    return;
-  }
-  // ordered compaction: process the bitmap in chunks of 256 entries
-  int32_t out = trow_ptr[g];
-  for (int base = 0; base < ntc; base += 256) {
-    const int i = base + threadIdx.x;
-    const uint32_t bits = i < ntc ? bitmap[i] : 0u;
-    const unsigned long long bal = __ballot(bits != 0u);
-    if (l == 0) wave_tot[w] = __popcll(bal);
-    __syncthreads();
-    int before = 0;
-    for (int k = 0; k < w; ++k) before += wave_tot[k];
-    const int total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-    if (bits) {
-      const int pos = out + before + (int)prefix_count(bal);
-      tcol[pos] = i;
-      tbits[pos] = bits;
-    }
-    out += total;
-    __syncthreads();
   }
 }
 
@@ -997,9 +1006,8 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
                           int32_t* trow_cnt, const int32_t* trow_ptr, int32_t* tcol,
                           uint32_t* tbits, hipStream_t s) {
   (void)nkb;
-  const size_t lds = (size_t)ntc * sizeof(uint32_t);
-  hipLaunchKernelGGL(k_coarsen, dim3(H * ntr), dim3(256), lds, s, row_ptr, cols, nqb, cq, ckv, ntr,
-                     ntc, trow_cnt, trow_ptr, tcol, tbits);
+  hipLaunchKernelGGL(k_coarsen, dim3(H * ntr), dim3(256), 0, s, row_ptr, cols, nqb, cq, ckv, ntr, ntc, trow_cnt,
+                     trow_ptr, tcol, tbits);
   return hipGetLastError();
 }
 

@@ -45,13 +45,15 @@ BOUNDS = {
     # head count: with many heads the task list spans far more K/V than the
     # caches hold, and organizations that keep neighbouring tiles together win
     "H": [16.0],
-    "N": [12288.0, 49152.0],
-    "density": [0.08, 0.2, 0.35],
-    "run_coverage": [0.5],
-    "row_skew": [2.0],
+    "N": [16384.0, 65536.0],
+    "density": [0.1, 0.25],
+    # run coverage and row skew are left to the decision-tree partition
+    "run_coverage": [],
+    "row_skew": [],
 }
 TOL_MAX, TOL_MEAN = 1e-2, 1e-3
 TOP = 6  # plans kept per regime ranking, before the base plan
+MIN_CASES = 8  # a regime's ranking rests on at least this many cases
 
 
 def bucket(bounds, x):
@@ -61,43 +63,37 @@ def bucket(bounds, x):
     return k
 
 
-def corpus(quick=False, extra=False):
-    """Profiling cases: (key, H, N, family, density target, seed).  Seeds start
-    at 900000 (base corpus) and 910000 (extra corpus), disjoint from the
-    benchmark workloads' (1000*c, 5000 + 10*r) and the held-out ablation
-    cases' (950000...).
+# request keys of the corpus: (B_Q, B_KV), head dim, largest N profiled
+KEYS = [((64, 64), 128, None), ((128, 128), 128, None), ((128, 32), 128, None), ((32, 128), 128, None),
+        ((64, 64), 64, 40960), ((16, 16), 128, 49152), ((32, 16), 128, 49152)]
+# two (H, N) sizes in every (head-count bucket, length bucket) cell
+SIZES = [(8, 8192), (4, 12288), (8, 16384), (4, 40960), (4, 75600), (2, 115200),
+         (24, 8192), (32, 12288), (24, 16384), (16, 49152), (24, 75600), (16, 115200)]
+# four target densities in every density bucket
+DENSITIES = [0.03, 0.05, 0.07, 0.09, 0.11, 0.15, 0.19, 0.23, 0.28, 0.35, 0.42, 0.5]
 
-    The extra corpus adds sizes and densities between the base corpus's, so
-    that a decision tree over the regime features finds enough cases per
-    leaf."""
-    keys = [((64, 64), 128), ((128, 128), 128), ((128, 32), 128), ((32, 128), 128), ((64, 64), 64)]
-    if quick:
-        sizes, dens = [(4, 8192), (2, 65536)], [0.1, 0.3]
-        big, big_dens = [(24, 32768)], [0.1]
-    elif extra:
-        sizes = [(12, 12288), (16, 16384), (8, 20480), (6, 28672), (4, 40960), (20, 49152), (3, 57344),
-                 (2, 81920)]
-        dens = [0.025, 0.045, 0.07, 0.09, 0.12, 0.16, 0.22, 0.3, 0.38, 0.48]
-        big, big_dens = [], []
-    else:
-        sizes = [(8, 8192), (8, 16384), (8, 32768), (4, 75600), (4, 115200)]
-        dens = [0.03, 0.06, 0.1, 0.14, 0.2, 0.28, 0.4, 0.5]
-        # many heads at long sequences (the second head-count bucket)
-        big, big_dens = [(24, 75600), (32, 115200)], [0.06, 0.14, 0.22]
+
+def corpus(quick=False):
+    """Profiling cases: (key, H, N, family, density target, seed).  Every
+    (head-count, length, density) bucket of a key gets two sizes times four
+    densities, so each fixed-interval regime rests on 8 cases; the mask
+    family rotates over the cases.  Seeds start at 920000, disjoint from the
+    benchmark workloads' (1000*c, 5000 + 10*r) and the held-out ablation
+    cases' (950000...)."""
+    sizes, dens = (SIZES[:1] + SIZES[6:7], DENSITIES[::4]) if quick else (SIZES, DENSITIES)
     families = ["clustered", "window", "iid_mixed", "iid"]
     cases = []
-    seed = 910000 if extra else 900000
-    for block, d in keys:
-        for grid, rhos in ((sizes, dens), (big, big_dens)):
-            for H, N in grid:
-                if d == 64 and N > 32768:
-                    continue
-                for i, rho in enumerate(rhos):
-                    fam = families[(i + N // 4096 + H) % 4] if extra else families[(i + N) % 4]
-                    if fam == "window" and block[0] != block[1]:
-                        fam = "clustered"
-                    cases.append(dict(block=block, d=d, H=H, N=N, family=fam, rho=rho, seed=seed))
-                    seed += 1
+    seed = 920000
+    for block, d, nmax in KEYS:
+        for si, (H, N) in enumerate(sizes):
+            if nmax is not None and N > nmax:
+                continue
+            for i, rho in enumerate(dens):
+                fam = families[(i + si) % 4]
+                if fam == "window" and block[0] != block[1]:
+                    fam = "clustered"
+                cases.append(dict(block=block, d=d, H=H, N=N, family=fam, rho=rho, seed=seed))
+                seed += 1
     return cases
 
 
@@ -147,9 +143,11 @@ def reference_rows(q, k, v, M, block, rows):
     return out
 
 
-def profile(cases, reps=5, warmup=3, log=print, plans=None):
+def profile(cases, reps=5, warmup=3, log=print, plans=None, save=None, done=()):
     """plans: optional regular expression; only catalog entries whose names
-    match it are profiled (to add new entries to existing records)."""
+    match it are profiled (to add new entries to existing records).  save:
+    called with the records so far after every case; done: records of an
+    earlier, interrupted run whose cases (by seed) are not profiled again."""
     import numpy as np
     import torch
 
@@ -157,8 +155,11 @@ def profile(cases, reps=5, warmup=3, log=print, plans=None):
     from workloads import gen
     dev = torch.device("cuda")
     cat = bsa.catalog()
-    records = []
+    records = list(done)
+    seen = {r["seed"] for r in records}
     for ci, c in enumerate(cases):
+        if c["seed"] in seen:
+            continue
         H, N, d = c["H"], c["N"], c["d"]
         BQ, BKV = c["block"]
         M = make_mask(c)
@@ -207,6 +208,8 @@ def profile(cases, reps=5, warmup=3, log=print, plans=None):
             f"best={cat[best]['name'] if best is not None else '-'} {lat.get(best, 0):.3f} ms")
         del q, k, v, out, Md
         torch.cuda.empty_cache()
+        if save:
+            save(records)
     return records
 
 
@@ -311,7 +314,9 @@ def compile_table(records, version, partition="intervals"):
             keyed.setdefault((r["block"][0], r["block"][1], r["d"]), []).append(r)
     lines = [f"bsa-plan-table {version}", "arch gfx950", f"catalog {bsa.catalog_hash()}"]
 
-    def emit(key, head, rs):
+    def emit(key, head, rs, min_cases=MIN_CASES):
+        if len(rs) < min_cases:
+            return  # too few cases: requests fall through to a coarser regime
         ranking, best = _ranking(bsa, key, rs)
         if ranking is None:
             return
@@ -326,7 +331,7 @@ def compile_table(records, version, partition="intervals"):
             rs = keyed[key]
             for tests, idx in tree_leaves(fit_tree(rs, depth)):
                 emit(key, ("rule", " ".join(f"{f}{op}{thr!r}" for f, op, thr in tests)), [rs[i] for i in idx])
-            emit(key, ("regime", " ".join(["*"] * 5)), rs)
+            emit(key, ("regime", " ".join(["*"] * 5)), rs, min_cases=1)
         return "\n".join(lines) + "\n"
 
     for f in ("H", "N", "density", "run_coverage", "row_skew"):
@@ -352,7 +357,7 @@ def compile_table(records, version, partition="intervals"):
         for (h, n) in sorted(coarse):
             emit(key, ("regime", " ".join([str(h) if BOUNDS["H"] else "*", str(n), "*", "*", "*"])),
                  coarse[(h, n)])
-        emit(key, ("regime", " ".join(["*"] * 5)), keyed[key])
+        emit(key, ("regime", " ".join(["*"] * 5)), keyed[key], min_cases=1)
     return "\n".join(lines) + "\n"
 
 
@@ -423,14 +428,12 @@ def choose_partition(records, log=print):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--out", default=os.path.join(HERE, "tables", "gfx950_v1.txt"))
+    ap.add_argument("--out", default=os.path.join(HERE, "tables", "gfx950_v2.txt"))
     ap.add_argument("--quick", action="store_true", help="small corpus (smoke test of the tool)")
     ap.add_argument("--version", default=None)
     ap.add_argument("--records", default=None, help="also write the profiling records (JSON) here")
     ap.add_argument("--from-records", default=None, nargs="+",
                     help="compile from saved records (no GPU); several files are concatenated")
-    ap.add_argument("--corpus", default="base", choices=["base", "extra", "all"],
-                    help="which synthetic corpus to profile")
     ap.add_argument("--shard", default=None, help="i/n: profile every n-th case starting at i")
     ap.add_argument("--plans", default=None, help="profile only catalog entries matching this regex")
     ap.add_argument("--partition", default="auto",
@@ -446,18 +449,23 @@ def main():
             r["block"] = tuple(r["block"])
             r["latency"] = {int(k): v for k, v in r["latency"].items()}
     else:
-        cases = []
-        if a.corpus in ("base", "all"):
-            cases += corpus(a.quick)
-        if a.corpus in ("extra", "all"):
-            cases += corpus(a.quick, extra=True)
+        cases = corpus(a.quick)
         if a.shard:
             i, n = (int(x) for x in a.shard.split("/"))
             cases = cases[i::n]
-        recs = profile(cases, log=lambda s: print(s, flush=True), plans=a.plans)
-        if a.records:
-            with open(a.records, "w") as f:
-                json.dump(recs, f)
+        done = []
+        if a.records and os.path.exists(a.records):
+            with open(a.records) as f:
+                done = json.load(f)  # resume an interrupted run
+
+        def save(rs):
+            if a.records:
+                with open(a.records + ".tmp", "w") as f:
+                    json.dump(rs, f)
+                os.replace(a.records + ".tmp", a.records)
+
+        recs = profile(cases, log=lambda s: print(s, flush=True), plans=a.plans, save=save, done=done)
+        save(recs)
     version = a.version or time.strftime("v1-%Y%m%d", time.gmtime())
     cvtext = ""
     if a.partition == "auto":

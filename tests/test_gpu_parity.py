@@ -43,7 +43,7 @@ def test_c1_every_eligible_plan(c1):
             p.destroy()
 
 
-GEOMS = [(64, 64), (128, 128), (128, 32), (32, 128), (64, 32), (32, 64)]
+GEOMS = [(64, 64), (128, 128), (128, 32), (32, 128), (64, 32), (32, 64), (16, 16), (16, 64), (32, 16)]
 
 
 @pytest.mark.parametrize("block", GEOMS)
@@ -145,4 +145,24 @@ def test_mask_state_matches_oracle(block, N):
     assert info["max_row_nnz"] == int(nnz_row.max())
     assert info["density"] == pytest.approx(ostats.density(M), abs=1e-12)
     assert info["run_coverage"] == pytest.approx(ostats.run_coverage(M), abs=1e-12)
+    p.destroy()
+
+
+def test_coarsened_row_wider_than_one_lds_window():
+    """A coarsened tile row with more tile columns (9,375) than the
+    coarsening kernel's LDS window (8,192): K/V coarsened x2 (B_KV = 16,
+    T_KV = 32), one head of 300,000 tokens.  Sampled rows against the oracle
+    and the whole tile coverage against the oracle's cells, bit-exact."""
+    H, N, d, block = 1, 300000, 64, (64, 16)
+    M, q, k, v = gen.random_case(H, N, d, *block, p=0.004, seed=4242)
+    pid = next(e["id"] for e in bsa.catalog() if e["name"] == "T64x32_d64_splitk")
+    p, out = gpu_run(M, q, k, v, block, force_plan=pid)
+    info = p.info
+    assert (info["coarsen_q"], info["coarsen_kv"]) == (1, 2)
+    rng = np.random.default_rng(4242)
+    rows = np.unique(np.concatenate([rng.integers(0, N, 200), np.arange(N - 64, N)]))
+    ref = oatt.attention_rows(q, k, v, M, *block, {0: rows})[0]
+    assert_close(out[0, torch.from_numpy(rows).cuda()], ref, "long coarsened row")
+    cov, cq, ckv = tile_cells(p, block, N)
+    assert (cov == coverage.cells(M, *block, N, cq, ckv)).all()
     p.destroy()

@@ -41,7 +41,7 @@ def test_forced_entry_repeats_use_the_speculative_list():
     set to a fresh build, and every output matches the oracle."""
     H, N, d, block = 2, 2003, 64, (64, 64)
     cat = bsa.catalog()
-    pid = next(e["id"] for e in cat if e["name"] == "T64x64_d64_splitk_lpt")
+    pid = next(e["id"] for e in cat if e["name"] == "T64x32_d64_splitk_xcd128")
     seen = []
     for i, rho in enumerate((0.2, 0.2, 0.5, 0.05)):
         M, q, k, v = gen.random_case(H, N, d, *block, p=rho, seed=8100 + i, empty_rows={0: [3]},
@@ -90,7 +90,7 @@ def test_speculative_list_with_batch_and_layout(layout, batch):
     list is speculative and the outputs match the oracle head by head."""
     H, N, d, block = 2, 1501, 128, (64, 64)
     Ht = batch * H
-    pid = next(e["id"] for e in bsa.catalog() if e["name"] == "T64x64_d128_splitk15_lpt")
+    pid = next(e["id"] for e in bsa.catalog() if e["name"] == "T64x64_d128_splitk_xcd")
     dev = torch.device("cuda")
     flags = []
     for i in range(3):
@@ -117,7 +117,7 @@ def test_speculative_list_for_a_large_mask():
     queued behind the scan): repeats take the speculative list, sampled rows
     match the oracle, and the task set equals a fresh build's."""
     H, N, d, block = 4, 20011, 64, (64, 64)
-    pid = next(e["id"] for e in bsa.catalog() if e["name"] == "T64x32_d64_splitk_lpt")
+    pid = next(e["id"] for e in bsa.catalog() if e["name"] == "T64x32_d64_nosplit_lpt")
     rng = np.random.default_rng(8400)
     dev = torch.device("cuda")
     flags, sets = [], []

@@ -72,11 +72,12 @@ def _expected_stream(rp, H, nqb, nqt_head, refine_q, G):
     return out, W, Ge
 
 
-CASES = [((64, 64), 40000, 8), ((128, 128), 9000, 6)]
+# (block, N, H, uncoarsened catalog entries that must be checked)
+CASES = [((64, 64), 40000, 8, 2), ((128, 128), 9000, 6, 6), ((128, 32), 20000, 6, 7)]
 
 
-@pytest.mark.parametrize("block,N,H", CASES)
-def test_task_organizations(block, N, H):
+@pytest.mark.parametrize("block,N,H,min_checked", CASES)
+def test_task_organizations(block, N, H, min_checked):
     d = 128
     M = gen.mask_clustered(H, N, *block, seed=4242 + N, rho=(0.05, 0.45), p_empty_head=0.25)
     nqb = M.shape[1]
@@ -129,10 +130,10 @@ def test_task_organizations(block, N, H):
                 f"{label}: max {err.max():.3e} mean {err.mean():.3e}"
         p.destroy()
         checked += 1
-    assert checked >= 6
+    assert checked >= min_checked
 
 
-@pytest.mark.parametrize("block,N,H", CASES + [((64, 64), 3000, 1)])
+@pytest.mark.parametrize("block,N,H", [c[:3] for c in CASES] + [((64, 64), 3000, 1)])
 def test_stream_organization(block, N, H):
     """force_split = SPLIT_STREAM: tasks are the tiles' intersections with G
     equal entry ranges (G = the plan's grid), in tile order; every range holds

@@ -25,11 +25,21 @@ def test_library_exports_header_symbols():
 
 
 def test_catalog_and_hash():
+    """The native catalog: 31 entries over 9 kernel tile shapes (the pages'
+    catalogs hold 14-26 entries per architecture), every shape with the
+    default organization that base plans use, every entry a distinct
+    (shape, organization)."""
     cat = bsa.catalog()
     shapes = {(e["tile_q"], e["tile_kv"], e["d"]) for e in cat}
     orgs = {(e["split"], e["xcd_remap"], e["order"]) for e in cat}
-    assert len(cat) == len(shapes) * len(orgs)  # every organization of every kernel shape
-    assert {(2, 0, 0), (0, 0, 0), (2, 16, 0), (2, 128, 0), (2, 0, 1), (3, 0, 1), (4, 0, 1), (0, 0, 1)} == orgs
+    assert len(cat) == 31 and len(shapes) == 9
+    assert orgs <= {(2, 0, 0), (0, 0, 0), (2, 16, 0), (2, 128, 0), (2, 0, 1), (3, 0, 1), (4, 0, 1), (0, 0, 1)}
+    for sh in shapes:
+        assert any((e["tile_q"], e["tile_kv"], e["d"]) == sh and (e["split"], e["xcd_remap"], e["order"]) == (2, 0, 0)
+                   for e in cat), sh
+    assert len({(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"], e["order"]) for e in cat}) == 31
+    per_d = {d: sum(1 for e in cat if e["d"] == d) for d in (64, 128)}
+    assert per_d == {64: 11, 128: 20}
     names = [e["name"] for e in cat]
     assert len(set(names)) == len(names)
     assert re.fullmatch(r"[0-9a-f]{16}", bsa.catalog_hash())
@@ -59,7 +69,7 @@ def test_lookup_miss_returns_base_plan(tmp_path):
 
 
 def test_builtin_table_is_versioned_and_covers_workload_keys():
-    assert bsa.table_version().startswith("v1")
+    assert bsa.table_version().startswith("v2")
     for H, N, d, block, dens, rc, sk in ((8, 8192, 128, (128, 128), 0.31, 0.5, 3.2),
                                          (40, 75600, 128, (64, 64), 0.13, 0.9, 1.3),
                                          (24, 115200, 128, (128, 32), 0.17, 0.86, 1.7),
@@ -73,8 +83,11 @@ def test_eligibility_rules():
     cat = bsa.catalog()
     by = {(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"]): e["id"] for e in cat
           if e["order"] == 0}
-    # coarsening B_Q = 16 into a 64-row tile would split a wave across logical rows
-    assert not bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 128, (16, 64))
+    # B_Q = 16 only inside coarsened query tiles (a wave's rows then span two
+    # logical rows, resolved per lane), within 32 membership bits
+    assert bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 128, (16, 64))      # 4 x 1 blocks
+    assert bsa.eligible(by[(128, 64, 128, 2, 0)], 1, 1024, 128, (16, 16))     # 8 x 4 blocks
+    assert not bsa.eligible(by[(128, 128, 128, 2, 0)], 1, 1024, 128, (16, 16))  # 8 x 8 > 32 bits
     assert bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 128, (32, 64))
     assert not bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 64, (64, 64))  # head dim
     assert bsa.eligible(by[(128, 32, 128, 2, 0)], 1, 1024, 128, (64, 128))  # mixed map
@@ -168,7 +181,7 @@ def test_layout_and_batch_validation():
     assert _create_status(mask_ptr=None, layout="NHD") == "BSA_ERR_INVALID_ARG"
     # block geometries outside the documented ranges are refused before any
     # launch (the mask pointer is never read)
-    assert _create_status(block=(16, 64)) == "BSA_ERR_UNSUPPORTED"
+    assert _create_status(block=(8, 64)) == "BSA_ERR_UNSUPPORTED"
     assert _create_status(block=(512, 64)) == "BSA_ERR_UNSUPPORTED"
     assert _create_status(block=(64, 8)) == "BSA_ERR_UNSUPPORTED"
     assert _create_status(block=(48, 64)) == "BSA_ERR_UNSUPPORTED"

@@ -28,7 +28,8 @@ def test_bucket_bounds():
     assert pt.bucket([], 3.0) == 0
 
 
-def test_geometric_mean_ranking_and_validity(tmp_path):
+def test_geometric_mean_ranking_and_validity(tmp_path, monkeypatch):
+    monkeypatch.setattr(pt, "MIN_CASES", 1)  # two cases make a regime here
     ids = _ids((128, 128))
     a, b, c = ids[0], ids[3], ids[6]
     # plan a: GM sqrt(1*4) = 2; plan b: GM sqrt(2*2) = 2.0 + tie-break by id; plan c: 1.5 but
@@ -70,16 +71,48 @@ def test_geometric_mean_ranking_and_validity(tmp_path):
         bsa.table_load(None)
 
 
-def test_cases_split_by_key_and_buckets():
+def test_cases_split_by_key_and_buckets(monkeypatch):
+    monkeypatch.setattr(pt, "MIN_CASES", 1)
     i128, i64 = _ids((128, 128)), _ids((64, 64))
     recs = [_rec((128, 128), 8192, 0.3, 0.6, 1.0, {i128[0]: 1.0}),
-            _rec((128, 128), 8192, 0.3, 0.6, 3.0, {i128[1]: 1.0}),   # row-skew bucket differs
+            _rec((128, 128), 8192, 0.05, 0.6, 3.0, {i128[1]: 1.0}),   # density bucket differs
             _rec((128, 128), 100000, 0.3, 0.6, 1.0, {i128[2]: 1.0}),  # N bucket differs
             _rec((128, 128), 8192, 0.3, 0.6, 1.0, {i128[3]: 1.0}, H=40),  # head-count bucket differs
             _rec((64, 64), 8192, 0.3, 0.6, 1.0, {i64[0]: 1.0})]       # key differs
     text = pt.compile_table(recs, "v2")
     fine = [ln for ln in text.splitlines() if ln.startswith("regime") and "*" not in ln]
     assert len(fine) == 5
+
+
+def test_regimes_rest_on_min_cases():
+    """A fixed-interval regime is emitted only with at least MIN_CASES cases;
+    fewer fall through to the coarser regimes (the key-wide one always
+    exists)."""
+    ids = _ids((128, 128))
+    few = [_rec((128, 128), 8192, 0.3, 0.6, 1.0, {ids[0]: 1.0, ids[1]: 2.0}) for _ in range(pt.MIN_CASES - 1)]
+    text = pt.compile_table(few, "vmin")
+    heads = [ln.split(" : ")[0].split()[4:] for ln in text.splitlines() if ln.startswith("regime")]
+    assert heads == [["*"] * 5]
+    enough = few + [_rec((128, 128), 8192, 0.31, 0.6, 1.0, {ids[0]: 1.0, ids[1]: 2.0})]
+    text = pt.compile_table(enough, "vmin")
+    heads = [ln.split(" : ")[0].split()[4:] for ln in text.splitlines() if ln.startswith("regime")]
+    assert len(heads) == 3 and "*" not in heads[0]
+
+
+def test_corpus_fills_every_interval_regime():
+    """Every (head-count, length, density) bucket of a key's profiled sizes
+    holds 2 sizes x 4 densities = 8 cases, or 4 where the key's length limit
+    keeps only one of the two sizes."""
+    import collections
+    cells = collections.Counter()
+    for c in pt.corpus():
+        cells[(c["block"], c["d"], pt.bucket(pt.BOUNDS["H"], c["H"]), pt.bucket(pt.BOUNDS["N"], c["N"]),
+               pt.bucket(pt.BOUNDS["density"], c["rho"]))] += 1
+    limits = {(b, d): n for b, d, n in pt.KEYS}
+    for (b, d, hb, nb, db), n in cells.items():
+        sizes = [s for s in pt.SIZES if pt.bucket(pt.BOUNDS["H"], s[0]) == hb and
+                 pt.bucket(pt.BOUNDS["N"], s[1]) == nb and (limits[(b, d)] is None or s[1] <= limits[(b, d)])]
+        assert n == 4 * len(sizes) and len(sizes) >= 1, (b, d, hb, nb, db)
 
 
 def test_corpus_seeds_disjoint_from_workloads():
@@ -162,12 +195,12 @@ def test_builtin_table_recompiles_from_its_records():
     import json
     import os
     tables = os.path.join(os.path.dirname(pt.__file__), "tables")
-    with open(os.path.join(tables, "gfx950_v1_records.json")) as f:
+    with open(os.path.join(tables, "gfx950_v2_records.json")) as f:
         recs = json.load(f)
     for r in recs:
         r["block"] = tuple(r["block"])
         r["latency"] = {int(k): v for k, v in r["latency"].items()}
-    with open(os.path.join(tables, "gfx950_v1.txt")) as f:
+    with open(os.path.join(tables, "gfx950_v2.txt")) as f:
         text = f.read()
     # the partition the shipped table was compiled with is the cross-validated choice
     part, _ = pt.choose_partition(recs, log=lambda s: None)
@@ -236,7 +269,7 @@ def test_tree_keeps_min_leaf_cases():
 
 
 def test_cross_validation_prefers_tree_off_the_fixed_bounds():
-    # 0.27 lies inside the fixed density bucket [0.2, 0.35): the intervals mix both regimes
+    # 0.27 lies inside the fixed density bucket [0.25, inf): the intervals mix both regimes
     recs, _, _ = _two_regime_records(0.27)
     cv = pt.cross_validate(recs, ["intervals", ("tree", 0), ("tree", 1)])
     assert cv[("tree", 1)] < cv["intervals"] and cv[("tree", 1)] < cv[("tree", 0)]
