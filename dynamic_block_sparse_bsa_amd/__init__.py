@@ -48,7 +48,7 @@ class PlanInfo(ctypes.Structure):
             "nnz_blocks", "n_tile_rows", "n_items", "n_tasks", "grid", "workspace_bytes",
             "long_run_blocks")] + \
         [(n, ctypes.c_double) for n in ("density", "run_coverage", "row_skew", "host_select_us")] + \
-        [("tasks_predicted", ctypes.c_int32)]
+        [("tasks_predicted", ctypes.c_int32), ("split_threshold", ctypes.c_int32)]
 
 
 class CatalogEntry(ctypes.Structure):

@@ -229,6 +229,7 @@ int wg_per_cu_cached(int tq, int tkv, int d, bool stream = false) {
 struct PlanShape {
   DimMap mq, mk;
   int split = 0;           // entries per partition, 0 = never split
+  int split_min = 0;       // rows of more entries are split
   int groups = 0;          // > 0: stream organization over this many workgroups
   int64_t tasks_upper = 0;
   int64_t slots_upper = 0;
@@ -246,7 +247,7 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
   // entries visited over all query tiles (upper bound for coarsened lists)
   const int64_t W = (int64_t)p.mq.refine * (int64_t)st.nnz;
   const int64_t row_max = (int64_t)p.mq.coarsen * st.max_row_nnz;
-  int split = 0;
+  int split = 0, split_min = 0;
   if (r.force_split == BSA_SPLIT_STREAM) {
     // one equal range of entries per resident workgroup slot
     const int64_t slots = (int64_t)device_cus(dev) * wg_per_cu_cached(e.tq, e.tkv, e.d, true);
@@ -257,13 +258,17 @@ PlanShape shape_plan(const CatalogEntry& e, const bsa_request& r, const MaskStat
     return p;
   }
   if (r.force_split > 0) {
-    split = r.force_split;
+    split = split_min = r.force_split;
   } else if (r.force_split < 0 && e.split) {
     const int64_t slots = (int64_t)device_cus(dev) * wg_per_cu_cached(e.tq, e.tkv, e.d);
     split = (int)std::max<int64_t>(4, cdiv(2 * std::max<int64_t>(W, 1), slots * e.split));
-    if (row_max <= split) split = 0;
+    // rows up to kSplitRowFactor times the mean row length stay whole
+    const int64_t mean = cdiv(std::max<int64_t>(W, 1), p.nqt);
+    split_min = (int)std::min<int64_t>(std::max<int64_t>(split, kSplitRowFactor * mean), 1 << 30);
+    if (row_max <= split_min) split = split_min = 0;
   }
   p.split = split;
+  p.split_min = split_min;
   if (split > 0) {
     p.tasks_upper = p.nqt + W / split + 1;
     p.slots_upper = 2 * W / split + 1;
@@ -818,7 +823,7 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
     TaskSpec ts;
     HIP_TRY(prepare_spec(ts));
     if (ts.enabled) {
-      HIP_TRY(launch_tasks((const int32_t*)p->row_ptr.ptr, ts.H, ts.nqt_head, ts.ntr, ts.refine_q, 0, ts.order, 0,
+      HIP_TRY(launch_tasks((const int32_t*)p->row_ptr.ptr, ts.H, ts.nqt_head, ts.ntr, ts.refine_q, 0, 0, ts.order, 0,
                            ts.parts, ts.slot_base, ts.tasks, dst, s, ts.dev_split, ts.slots, ts.split_tiles));
       spec_launched = true;
     }
@@ -949,7 +954,8 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
     std::swap(p->split_tiles, p->spec_split);
   } else {
     if (shape.split > 0) HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)nqt, &p->split_tiles));
-    HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split, chosen->order,
+    HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split, shape.split_min,
+                         chosen->order,
                          (int32_t)max_len, (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr,
                          (Task*)p->tasks.ptr, dst, s, -1, 0, (int32_t*)p->split_tiles.ptr));
   }
@@ -970,6 +976,7 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
   in.refine_q = shape.mq.refine;
   in.refine_kv = shape.mk.refine;
   in.split_items = shape.split;
+  in.split_threshold = shape.split_min;
   in.max_row_nnz = (int32_t)p->stats.max_row_nnz;
   in.nnz_blocks = (int64_t)p->stats.nnz;
   in.n_tile_rows = (int64_t)r.H * p->ntr;

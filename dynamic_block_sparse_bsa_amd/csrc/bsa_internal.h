@@ -166,13 +166,17 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
                           int32_t nkb, int32_t cq, int32_t ckv, int32_t ntr, int32_t ntc,
                           int32_t* trow_cnt, const int32_t* trow_ptr, int32_t* tcol,
                           uint32_t* tbits, hipStream_t s);
-// dev_split >= 0: split and max_len are derived on the device from *st (the
-// balance rule with split share dev_split in halves over `slots` workgroups,
-// uncoarsened tile list); -1: the given split and max_len are used.
-// split_tiles (nullable): receives the query tiles with more than one
+// A query tile's row of n > split_min entries is cut into ceil(n / split)
+// partitions.  dev_split >= 0: split, split_min and max_len are derived on
+// the device from *st (the balance rule with split share dev_split in halves
+// over `slots` workgroups, uncoarsened tile list); -1: the given values are
+// used.  split_tiles (nullable): receives the query tiles with more than one
 // partition, ascending; their count goes to st->n_split.
+// The balance rule leaves rows of up to kSplitRowFactor times the mean row
+// length whole: cutting rows of an even mask only adds partials to merge.
+constexpr int kSplitRowFactor = 2;
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
-                        int32_t refine_q, int32_t split, int32_t order, int32_t max_len,
+                        int32_t refine_q, int32_t split, int32_t split_min, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
                         hipStream_t s, int32_t dev_split = -1, int32_t slots = 0,
                         int32_t* split_tiles = nullptr);

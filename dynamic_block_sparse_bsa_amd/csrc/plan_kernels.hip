@@ -361,7 +361,7 @@ __device__ inline uint32_t nz_bits16(const u32x4v x) {
 // are the columns compacted from the bitmap, so the host's plan selection
 // overlaps the compaction.  Same outputs as k_row_count + k_scan + k_compact.
 __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr, int32_t refine_q,
-                            int32_t split, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
+                            int32_t split, int32_t split_min, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
                             int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
                             int32_t dev_split, int32_t slots, int32_t* __restrict__ split_tiles,
                             unsigned long long stat_nnz, unsigned stat_max_row);
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__
   if (spec.enabled) {
     // the speculative task list, from the row offsets in LDS
     __syncthreads();
-    build_tasks(off, spec.H, spec.nqt_head, spec.ntr, spec.refine_q, 0, spec.order, 0, spec.parts,
+    build_tasks(off, spec.H, spec.nqt_head, spec.ntr, spec.refine_q, 0, 0, spec.order, 0, spec.parts,
                 spec.slot_base, spec.tasks, st, spec.dev_split, spec.slots, spec.split_tiles, s_nnz, s_maxrow);
   }
   // column compaction, one thread per (row, 32-column word): the word's
@@ -599,7 +599,7 @@ struct RowTasks {
 };
 
 __device__ inline RowTasks row_tasks(const int32_t* __restrict__ trow_ptr, int g, int nqt_head,
-                                     int ntr, int refine_q, int split) {
+                                     int ntr, int refine_q, int split, int split_min) {
   RowTasks r;
   r.h = g / nqt_head;
   r.qt = g - r.h * nqt_head;
@@ -607,7 +607,7 @@ __device__ inline RowTasks row_tasks(const int32_t* __restrict__ trow_ptr, int g
   r.b = trow_ptr[r.h * ntr + tr];
   r.e = trow_ptr[r.h * ntr + tr + 1];
   const int n = r.e - r.b;
-  r.p = (split > 0 && n > split) ? (n + split - 1) / split : 1;
+  r.p = (split > 0 && n > split_min) ? (n + split - 1) / split : 1;
   r.chunk = (n + r.p - 1) / r.p;
   return r;
 }
@@ -631,16 +631,17 @@ __device__ inline Task make_task(const RowTasks& r, int i, int slot0) {
 }
 
 //
-// dev_split >= 0: split and max_len are not given but derived here from the
-// statistics in *st with the host's balance rule for a plan of split share
-// dev_split (in halves; 0 = never split) over `slots` resident workgroups
-// and an uncoarsened tile list, so the builder can be queued before the host
-// has read the statistics.
+// A row of n > split_min entries is cut into ceil(n / split) partitions.
+// dev_split >= 0: split, split_min and max_len are not given but derived here
+// from the statistics in *st with the host's balance rule for a plan of
+// split share dev_split (in halves; 0 = never split) over `slots` resident
+// workgroups and an uncoarsened tile list, so the builder can be queued
+// before the host has read the statistics.
 // The builder runs in one workgroup of 1024 threads: as its own kernel
 // (k_tasks) or inside k_mask_small.  stat_nnz / stat_max_row are the
 // statistics the device split rule reads (dev_split >= 0).
 __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr, int32_t refine_q,
-                            int32_t split, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
+                            int32_t split, int32_t split_min, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
                             int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
                             int32_t dev_split, int32_t slots, int32_t* __restrict__ split_tiles,
                             unsigned long long stat_nnz, unsigned stat_max_row) {
@@ -651,13 +652,16 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
   if (dev_split >= 0) {
     const long long W = (long long)refine_q * (long long)stat_nnz;
     const long long row_max = (long long)stat_max_row;
-    long long sp = 0;
+    long long sp = 0, smin = 0;
     if (dev_split > 0) {
       const long long den = (long long)slots * dev_split;
       sp = max(4LL, (2 * max(W, 1LL) + den - 1) / den);
-      if (row_max <= sp) sp = 0;
+      const long long mean = (max(W, 1LL) + nqt - 1) / nqt;
+      smin = max(sp, kSplitRowFactor * mean);
+      if (row_max <= smin) sp = 0;
     }
     split = (int32_t)sp;
+    split_min = (int32_t)min(smin, (long long)(1 << 30));
     max_len = sp > 0 ? (int32_t)sp : (int32_t)min(row_max, (long long)(1 << 30));
   }
   max_len = max(max_len, 1);
@@ -676,7 +680,7 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
     for (int k = 0; k < 4; ++k) {
       r[k].p = 0;
       if (g0 + k < nqt) {
-        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split);
+        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split, split_min);
         sum_t += r[k].p;
         sum_s += r[k].p > 1 ? r[k].p : 0;
       }
@@ -743,7 +747,7 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
       for (int k = 0; k < 4; ++k) {
         r[k].p = 0;
         if (g0 + k < nqt) {
-          r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split);
+          r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split, split_min);
           sum_s += r[k].p > 1 ? r[k].p : 0;
         }
       }
@@ -765,16 +769,16 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
 
 __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow_ptr, int32_t H,
                                                 int32_t nqt_head, int32_t ntr, int32_t refine_q,
-                                                int32_t split, int32_t order, int32_t max_len,
-                                                int32_t* __restrict__ parts,
+                                                int32_t split, int32_t split_min, int32_t order,
+                                                int32_t max_len, int32_t* __restrict__ parts,
                                                 int32_t* __restrict__ slot_base,
                                                 Task* __restrict__ tasks, MaskStats* st,
                                                 int32_t dev_split, int32_t slots,
                                                 int32_t* __restrict__ split_tiles) {
   const unsigned long long nnz = dev_split >= 0 ? st->nnz : 0ull;
   const unsigned max_row = dev_split >= 0 ? st->max_row_nnz : 0u;
-  build_tasks(trow_ptr, H, nqt_head, ntr, refine_q, split, order, max_len, parts, slot_base, tasks, st,
-              dev_split, slots, split_tiles, nnz, max_row);
+  build_tasks(trow_ptr, H, nqt_head, ntr, refine_q, split, split_min, order, max_len, parts, slot_base, tasks,
+              st, dev_split, slots, split_tiles, nnz, max_row);
 }
 
 // Stream organization: the concatenated entries of all query tiles (head,
@@ -809,7 +813,7 @@ __global__ __launch_bounds__(1024) void k_tasks_stream(const int32_t* __restrict
     for (int k = 0; k < 4; ++k) {
       const int g = base + 4 * t + k;
       if (g < nqt) {
-        const RowTasks r = row_tasks(trow_ptr, g, nqt_head, ntr, refine_q, 0);
+        const RowTasks r = row_tasks(trow_ptr, g, nqt_head, ntr, refine_q, 0, 0);
         sum += r.e - r.b;
       }
     }
@@ -833,7 +837,7 @@ __global__ __launch_bounds__(1024) void k_tasks_stream(const int32_t* __restrict
       r[k].p = 0;
       r[k].b = r[k].e = 0;
       if (g0 + k < nqt) {
-        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, 0);
+        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, 0, 0);
         sum_n += r[k].e - r[k].b;
       }
     }
@@ -1021,11 +1025,11 @@ hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_h
 }
 
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
-                        int32_t refine_q, int32_t split, int32_t order, int32_t max_len,
+                        int32_t refine_q, int32_t split, int32_t split_min, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
                         hipStream_t s, int32_t dev_split, int32_t slots, int32_t* split_tiles) {
   hipLaunchKernelGGL(k_tasks, dim3(1), dim3(1024), 0, s, trow_ptr, H, nqt_head, ntr, refine_q, split,
-                     order, max_len, parts, slot_base, tasks, st, dev_split, slots, split_tiles);
+                     split_min, order, max_len, parts, slot_base, tasks, st, dev_split, slots, split_tiles);
   return hipGetLastError();
 }
 

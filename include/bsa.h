@@ -115,6 +115,11 @@ typedef struct {
                               entry this request key selected last time, queued
                               before the statistics reached the host, and the
                               selection agreed; 0: built after the selection */
+  int32_t split_threshold; /* rows (query tiles' tile-list rows) of more entries
+                              than this are split into partitions of at most
+                              split_items entries; 0 = no split (section 4.3
+                              leaves the rule open: the balance rule keeps rows
+                              of up to twice the mean length whole)          */
 } bsa_plan_info;
 
 /* Description of one catalog entry (paper section 4.4: native catalog). */

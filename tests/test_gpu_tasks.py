@@ -33,14 +33,14 @@ from bsa_testutil import MAX_ERR, MEAN_ERR
 pytestmark = pytest.mark.gpu
 
 
-def _expected_tasks(rp, H, nqb, nqt_head, refine_q, split):
+def _expected_tasks(rp, H, nqb, nqt_head, refine_q, split, split_min):
     out = []
     for h in range(H):
         for qt in range(nqt_head):
             i = h * nqb + qt // refine_q
             b, e = int(rp[i]), int(rp[i + 1])
             n = e - b
-            p = -(-n // split) if (split > 0 and n > split) else 1
+            p = -(-n // split) if (split > 0 and n > split_min) else 1
             ch = -(-n // p)
             for j in range(p):
                 out.append((h, qt, min(e, b + j * ch), min(e, b + (j + 1) * ch), p > 1))
@@ -96,7 +96,13 @@ def test_task_organizations(block, N, H, min_checked):
         rp, _ = p.export_csr()
         head, qt, beg, end, slot = p.export_tasks()
         nqt_head = -(-N // info["tile_q"])
-        exp = _expected_tasks(rp, H, nqb, nqt_head, info["refine_q"], info["split_items"])
+        label_pre = f"{e['name']} B={block} N={N}: split threshold"
+        exp = _expected_tasks(rp, H, nqb, nqt_head, info["refine_q"], info["split_items"],
+                              info["split_threshold"])
+        if info["split_items"] > 0:
+            # the balance rule keeps rows of up to twice the mean length whole
+            mean = -(-int(rp[-1]) * info["refine_q"] // (H * nqt_head))
+            assert info["split_threshold"] == max(info["split_items"], 2 * mean), label_pre
         got = list(zip(head.tolist(), qt.tolist(), beg.tolist(), end.tolist(), (slot >= 0).tolist()))
         label = f"{e['name']} B={block} N={N}"
         assert sorted(got) == sorted(exp), f"{label}: task multiset"
