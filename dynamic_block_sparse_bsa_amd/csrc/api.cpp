@@ -371,7 +371,8 @@ bsa_status validate_request(const bsa_request* rq) {
     return fail(BSA_ERR_UNSUPPORTED, "N * row stride too large for layout %d", rq->layout);
   const bsa_request fr = folded(*rq);
   const bsa_request* r = &fr;
-  if (r->d != 64 && r->d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim %d unsupported (64, 128)", r->d);
+  if (r->d != 32 && r->d != 64 && r->d != 128 && r->d != 256)
+    return fail(BSA_ERR_UNSUPPORTED, "head dim %d unsupported (32, 64, 128, 256)", r->d);
   if (!pow2(r->block_q) || r->block_q < 16 || r->block_q > 256)
     return fail(BSA_ERR_UNSUPPORTED, "block_q %d unsupported (power of two in [16, 256])", r->block_q);
   if (!pow2(r->block_kv) || r->block_kv < 16 || r->block_kv > 256)

@@ -66,17 +66,20 @@ struct AttnShape {
   static_assert(TQ % 32 == 0 && TKV % 32 == 0 && D % 32 == 0, "shape");
 };
 
-// 16-byte chunk swizzle of a row-major [rows][D] bf16 tile in LDS.  For D=128
-// (16 chunks = 256 B per row) the two 2-bit fields of row%16 are swapped into
-// the chunk index; for D=64 (two rows per 256 B) row/2 is XORed in.  Both the
+// 16-byte chunk swizzle of a row-major [rows][D] bf16 tile in LDS.  A 16-byte
+// chunk's bank group is its byte address / 16 mod 16.  For D >= 128 (rows of
+// 256 or 512 B, so the group is the chunk index mod 16) the two 2-bit fields
+// of row%16 are swapped into the chunk index; for D=64 (two rows per 256 B)
+// row/2 is XORed in; for D=32 (four rows per 256 B) (row/4)%4.  Both the
 // QK^T A-operand reads (ds_read_b128, 16 consecutive permuted rows per lane
 // group) and the PV transposed reads (ds_read_b64_tr_b16, 8 rows x 4 chunks
 // per instruction half) then hit every 16-byte bank group at most the
 // minimum number of times.
 template <int D>
 __device__ __forceinline__ int chunk_swz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return (row >> 1) & 7;
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else if constexpr (D == 64) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
 }
 
 template <int D>

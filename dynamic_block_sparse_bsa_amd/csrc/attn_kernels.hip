@@ -16,6 +16,12 @@ AttnLauncher attn_launcher(int tq, int tkv, int d) {
   BSA_CASE(64, 64, 64)
   BSA_CASE(128, 32, 64)
   BSA_CASE(128, 64, 64)
+  BSA_CASE(64, 32, 32)
+  BSA_CASE(64, 64, 32)
+  BSA_CASE(128, 64, 32)
+  BSA_CASE(128, 128, 32)
+  BSA_CASE(64, 32, 256)
+  BSA_CASE(128, 32, 256)
 #undef BSA_CASE
   return nullptr;
 }
@@ -49,6 +55,12 @@ int attn_wg_per_cu(int tq, int tkv, int d, bool stream) {
   BSA_CASE(64, 64, 64)
   BSA_CASE(128, 32, 64)
   BSA_CASE(128, 64, 64)
+  BSA_CASE(64, 32, 32)
+  BSA_CASE(64, 64, 32)
+  BSA_CASE(128, 64, 32)
+  BSA_CASE(128, 128, 32)
+  BSA_CASE(64, 32, 256)
+  BSA_CASE(128, 32, 256)
 #undef BSA_CASE
   return 0;
 }

@@ -37,10 +37,10 @@ constexpr Org kSplitKXcd128 = {"splitk_xcd128", 2, kXcdRunLong, 0};
 std::vector<CatalogEntry> build_catalog() {
   // Kernel tile shapes instantiated for gfx950 (attn_kernels.hip) and the
   // organizations offered with each.  Every shape has the default
-  // organization (a key's base plan uses it); the others were kept where
-  // they were the fastest plan on some profiling cases: of 104 shape x
-  // organization entries, dropping all but these 31 raised the corpus's
-  // best-achievable geometric-mean latency by under 0.1%.
+  // organization (a key's base plan uses it); at d = 64 and 128 the others
+  // were kept where they were the fastest plan on some profiling cases: of
+  // 104 shape x organization entries, dropping all but these 31 raised the
+  // corpus's best-achievable geometric-mean latency by under 0.1%.
   struct Shape {
     int tq, tkv, d;
     std::vector<Org> orgs;
@@ -55,6 +55,14 @@ std::vector<CatalogEntry> build_catalog() {
       {64, 32, 64, {kSplitK, kNoSplitLpt, kSplitKXcd128}},
       {128, 32, 64, {kSplitK, kNoSplitLpt}},
       {128, 64, 64, {kSplitK, kNoSplitLpt, kSplitKLpt, kSplitK2Lpt, kSplitKXcd}},
+      // further head dimensions (request property x, section 4.4), default
+      // organization only (no profiled regimes: their requests use the base plan)
+      {64, 32, 32, {kSplitK}},
+      {64, 64, 32, {kSplitK}},
+      {128, 64, 32, {kSplitK}},
+      {128, 128, 32, {kSplitK}},
+      {64, 32, 256, {kSplitK}},
+      {128, 32, 256, {kSplitK}},
   };
   std::vector<CatalogEntry> c;
   for (const Shape& sh : shapes) {

@@ -67,7 +67,7 @@ typedef struct bsa_plan bsa_plan;
 typedef struct {
   int32_t H;         /* heads per batch entry, >= 1                             */
   int32_t N;         /* sequence length (queries = keys), >= 1                  */
-  int32_t d;         /* head dimension: 64 or 128                               */
+  int32_t d;         /* head dimension: 32, 64, 128 or 256                      */
   int32_t block_q;   /* B_Q: 16, 32, 64, 128 or 256                             */
   int32_t block_kv;  /* B_KV: 16, 32, 64, 128 or 256                            */
   int32_t dtype;     /* BSA_DTYPE_BF16                                          */

@@ -47,10 +47,10 @@ GEOMS = [(64, 64), (128, 128), (128, 32), (32, 128), (64, 32), (32, 64), (16, 16
 
 
 @pytest.mark.parametrize("block", GEOMS)
-@pytest.mark.parametrize("N,d", [(777, 128), (1024, 128), (777, 64), (1000, 64)])
+@pytest.mark.parametrize("N,d", [(777, 128), (1024, 128), (777, 64), (1000, 64), (777, 32), (1000, 256)])
 def test_small_all_plans(block, N, d):
-    """Every eligible plan x split mode on small ragged and aligned cases, both
-    head dims, square and non-square B: output parity and exact coverage."""
+    """Every eligible plan x split mode on small ragged and aligned cases, every
+    head dim, square and non-square B: output parity and exact coverage."""
     H = 3
     seed = 100 + block[0] + 7 * block[1] + N + d
     M, q, k, v = gen.random_case(H, N, d, *block, p=0.3, seed=seed,
@@ -68,7 +68,7 @@ def test_small_all_plans(block, N, d):
 
 
 @pytest.mark.parametrize("std", [2.0, 3.0])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_sharp_scores(std, d):
     """Q and K with standard deviation 2-3 (sharply peaked softmax, as in
     trained attention layers): scores span tens of units, so an extra bf16

@@ -25,21 +25,22 @@ def test_library_exports_header_symbols():
 
 
 def test_catalog_and_hash():
-    """The native catalog: 31 entries over 9 kernel tile shapes (the pages'
-    catalogs hold 14-26 entries per architecture), every shape with the
+    """The native catalog: 37 entries over 15 kernel tile shapes (31 entries
+    at d = 64 and 128, where the pages' catalogs hold 14-26 entries per
+    architecture, plus one per shape at d = 32 and 256), every shape with the
     default organization that base plans use, every entry a distinct
     (shape, organization)."""
     cat = bsa.catalog()
     shapes = {(e["tile_q"], e["tile_kv"], e["d"]) for e in cat}
     orgs = {(e["split"], e["xcd_remap"], e["order"]) for e in cat}
-    assert len(cat) == 31 and len(shapes) == 9
+    assert len(cat) == 37 and len(shapes) == 15
     assert orgs <= {(2, 0, 0), (0, 0, 0), (2, 16, 0), (2, 128, 0), (2, 0, 1), (3, 0, 1), (4, 0, 1), (0, 0, 1)}
     for sh in shapes:
         assert any((e["tile_q"], e["tile_kv"], e["d"]) == sh and (e["split"], e["xcd_remap"], e["order"]) == (2, 0, 0)
                    for e in cat), sh
-    assert len({(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"], e["order"]) for e in cat}) == 31
-    per_d = {d: sum(1 for e in cat if e["d"] == d) for d in (64, 128)}
-    assert per_d == {64: 11, 128: 20}
+    assert len({(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"], e["order"]) for e in cat}) == 37
+    per_d = {d: sum(1 for e in cat if e["d"] == d) for d in (32, 64, 128, 256)}
+    assert per_d == {32: 4, 64: 11, 128: 20, 256: 2}
     names = [e["name"] for e in cat]
     assert len(set(names)) == len(names)
     assert re.fullmatch(r"[0-9a-f]{16}", bsa.catalog_hash())
@@ -91,6 +92,16 @@ def test_eligibility_rules():
     assert bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 128, (32, 64))
     assert not bsa.eligible(by[(64, 64, 128, 2, 0)], 1, 1024, 64, (64, 64))  # head dim
     assert bsa.eligible(by[(128, 32, 128, 2, 0)], 1, 1024, 128, (64, 128))  # mixed map
+    # head dims 32 and 256 (request property x, Tessera section 4.4)
+    assert bsa.eligible(by[(64, 64, 32, 2, 0)], 1, 1024, 32, (64, 64))
+    assert not bsa.eligible(by[(64, 64, 32, 2, 0)], 1, 1024, 64, (64, 64))
+    assert bsa.eligible(by[(64, 32, 256, 2, 0)], 1, 1024, 256, (64, 64))
+    assert bsa.eligible(by[(128, 32, 256, 2, 0)], 1, 1024, 256, (128, 32))
+    assert not bsa.eligible(by[(128, 32, 256, 2, 0)], 1, 1024, 128, (128, 32))
+    for d in (32, 256):
+        for block in ((64, 64), (128, 128), (128, 32), (32, 128)):
+            e = {c["id"]: c for c in cat}[bsa.base_plan(4, 4096, d, block)]
+            assert e["d"] == d and (e["split"], e["xcd_remap"], e["order"]) == (2, 0, 0)
 
 
 def test_unsupported_request_errors():
@@ -186,6 +197,7 @@ def test_layout_and_batch_validation():
     assert _create_status(block=(64, 8)) == "BSA_ERR_UNSUPPORTED"
     assert _create_status(block=(48, 64)) == "BSA_ERR_UNSUPPORTED"
     assert _create_status(d=96) == "BSA_ERR_UNSUPPORTED"
+    assert _create_status(d=512) == "BSA_ERR_UNSUPPORTED"
     with pytest.raises(bsa.BsaError):
         bsa.tensor_shapes(4, 1024, 128, layout="HDN")
 
