@@ -133,15 +133,18 @@ typedef struct {
   char name[48];
 } bsa_catalog_entry;
 
-/* Create a plan for a request.  Builds the mask state on `stream`, copies the
- * statistics to the host (the single synchronization of the request path),
- * selects the plan and prepares its metadata on `stream`.  On BSA_OK, *out
+/* Create a plan for a request (paper section 3, "Online request path";
+ * section 5.2: mask state, regime lookup, ranked fallback, launch
+ * preparation).  Builds the mask state on `stream`, copies the statistics to
+ * the host (the single synchronization of the request path), selects the
+ * plan and prepares its metadata on `stream`.  On BSA_OK, *out
  * owns device memory until bsa_plan_destroy.  Errors: BSA_ERR_INVALID_ARG
  * (null pointers, non-positive sizes), BSA_ERR_UNSUPPORTED (dtype, layout,
  * d, geometry or forced plan not eligible), BSA_ERR_NO_MEMORY, BSA_ERR_HIP. */
 bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out);
 
-/* Run a prepared plan: O = BSA(Q, K, V).  Q, K, V, O are device bf16
+/* Run a prepared plan: O = BSA(Q, K, V) (paper section 2.3: the attention
+ * mainloop over the plan's tiles; section 4.3: the split-K merge).  Q, K, V, O are device bf16
  * buffers of batch * H * N * d elements in the request's layout; O is fully
  * written (zeros for empty rows).  Stream-ordered and asynchronous.  One run per plan may be in
  * flight at a time (the split-K workspace is per plan).  Q/K/V may alias each
@@ -150,7 +153,7 @@ bsa_status bsa_run(const bsa_plan* plan, const void* q, const void* k, const voi
                    void* stream);
 
 /* Same as bsa_run, and also returns the attention kernel's own duration in
- * milliseconds, measured with HIP events recorded on `stream` around that
+ * milliseconds (kernel latency in the sense of paper section 7.1), measured with HIP events recorded on `stream` around that
  * launch (the call synchronizes on the end event). */
 bsa_status bsa_run_timed(const bsa_plan* plan, const void* q, const void* k, const void* v,
                          void* o, void* stream, float* attn_ms, float* merge_ms);
@@ -178,15 +181,20 @@ bsa_status bsa_run_timed(const bsa_plan* plan, const void* q, const void* k, con
 bsa_status bsa_attention_noalloc(const bsa_request* req, const void* q, const void* k, const void* v,
                                  void* o, void* stream);
 
-/* Release a plan.  Waits for the plan's latest stream work (its creation or
+/* Release a plan and the metadata it prepared (paper section 5.2, "Launch
+ * preparation").  Waits for the plan's latest stream work (its creation or
  * its most recent run) first; runs must not be in flight on other streams.
  * NULL is accepted. */
 bsa_status bsa_plan_destroy(bsa_plan* plan);
 
-/* Copy the plan's scalar facts to *info (host). */
+/* Copy the plan's scalar facts to *info (host): the plan tuple
+ * <g_Q, g_KV, sigma, e> of paper section 4.1 as chosen, plus the request's
+ * mask statistics (section 5.1). */
 bsa_status bsa_plan_get_info(const bsa_plan* plan, bsa_plan_info* info);
 
-/* Export the physical tiles the attention kernels will visit, in task order,
+/* Export the physical tiles the attention kernels will visit (paper section
+ * 2.2: a plan must cover exactly the interactions E(M); section 4.2: the
+ * Direct, Coarsened and Refined mappings), in task order,
  * to host arrays of capacity `cap` records: head, query-tile index, K/V tile
  * index (in units of T_Q and T_KV tokens) and the membership bits of the
  * tile (bit a*coarsen_kv + b set = logical block (a, b) inside the tile is
@@ -208,12 +216,13 @@ bsa_status bsa_plan_export_tasks(const bsa_plan* plan, int32_t* head, int32_t* q
                                  int32_t* begin, int32_t* end, int32_t* slot, int64_t cap,
                                  int64_t* count);
 
-/* Copy the shared block-CSR (row offsets [H*ceil(N/B_Q)+1] and column
- * indices [nnz_blocks]) to host arrays. */
+/* Copy the shared block-CSR (paper section 3 and section 5.2: the mask state
+ * mu(M) every plan of the request reads; row offsets [H*ceil(N/B_Q)+1] and
+ * column indices [nnz_blocks]) to host arrays. */
 bsa_status bsa_plan_export_csr(const bsa_plan* plan, int32_t* row_ptr, int32_t* cols,
                                int64_t cap_cols);
 
-/* Catalog introspection. */
+/* Catalog introspection (paper section 4.4: the native catalog C_A). */
 int32_t bsa_catalog_size(void);
 bsa_status bsa_catalog_get(int32_t id, bsa_catalog_entry* out);
 
@@ -276,15 +285,19 @@ bsa_status bsa_plan_cache_run(bsa_plan_cache* cache, const bsa_request* req, con
 /* Destroys every cached plan (after their latest stream work) and the cache. */
 bsa_status bsa_plan_cache_destroy(bsa_plan_cache* cache);
 
-/* Load a versioned plan table (text artifact) replacing the built-in one.
+/* Load a versioned plan table (text artifact; paper section 5.1: the regime
+ * table compiled offline per architecture) replacing the built-in one.
  * BSA_ERR_TABLE if unreadable, malformed, or built for another architecture
  * or catalog.  NULL restores the built-in table. */
 bsa_status bsa_table_load(const char* path);
 
-/* Version strings of the loaded table and of the catalog. */
+/* Version strings of the loaded table and of the catalog (the versioning of
+ * paper section 5.1's table against section 4.4's catalog). */
 const char* bsa_table_version(void);
 const char* bsa_catalog_hash(void);
 
+/* Error reporting (library utilities with no counterpart in the paper):
+ * the name of a status code, and the calling thread's last error message. */
 const char* bsa_status_string(int32_t status);
 const char* bsa_last_error(void);
 
