@@ -571,9 +571,11 @@ PredKey pred_key(int dev, const bsa_request& r) {
 }
 
 // The entry can be predicted: uncoarsened in both dimensions and organized
-// by k_tasks with the plan's own split rule or none.
+// by k_tasks with the plan's own split rule or none, in an order that needs
+// no column list (the speculative builder runs before the compaction).
 bool predictable(const CatalogEntry& e, const bsa_request& r) {
   if (r.force_split != -1 && r.force_split != 0) return false;
+  if (e.order == 2) return false;
   const DimMap mq = map_dim(r.block_q, e.tq, kMinCoarsenBlockQ), mk = map_dim(r.block_kv, e.tkv, 1);
   return mq.ok && mk.ok && mq.coarsen == 1 && mk.coarsen == 1;
 }
@@ -958,7 +960,8 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
     HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split, shape.split_min,
                          chosen->order,
                          (int32_t)max_len, (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr,
-                         (Task*)p->tasks.ptr, dst, s, -1, 0, (int32_t*)p->split_tiles.ptr));
+                         (Task*)p->tasks.ptr, dst, s, -1, 0, (int32_t*)p->split_tiles.ptr, p->tcol,
+                         (int32_t)cdiv(p->nkb, ckv)));
   }
   if (!arena) pred_store(pkey, predictable(*chosen, r) && shape.groups == 0 ? chosen->id : -1);
   if (shape.slots_upper > 0) HIP_TRY(p->alloc((size_t)shape.ws_bytes, &p->ws));

@@ -174,12 +174,14 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
 // partition, ascending; their count goes to st->n_split.
 // The balance rule leaves rows of up to kSplitRowFactor times the mean row
 // length whole: cutting rows of an even mask only adds partials to merge.
+// order: 0 query-tile order, 1 longest first, 2 by head and column signature
+// (needs the tile list's columns tcol and their count ncol).
 constexpr int kSplitRowFactor = 2;
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t split_min, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
                         hipStream_t s, int32_t dev_split = -1, int32_t slots = 0,
-                        int32_t* split_tiles = nullptr);
+                        int32_t* split_tiles = nullptr, const int32_t* tcol = nullptr, int32_t ncol = 0);
 // With a.split_tiles, grid_items (> 0) workgroups loop over the listed
 // (tile, column group) items; otherwise one workgroup per (query tile,
 // column group).  A column group is kMergeCols output columns.

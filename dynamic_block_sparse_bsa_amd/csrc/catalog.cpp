@@ -33,6 +33,8 @@ constexpr Org kSplitKXcd = {"splitk_xcd", 2, kXcdRun, 0};
 constexpr Org kSplitK15Lpt = {"splitk15_lpt", 3, 0, 1};
 constexpr Org kSplitK2Lpt = {"splitk2_lpt", 4, 0, 1};
 constexpr Org kSplitKXcd128 = {"splitk_xcd128", 2, kXcdRunLong, 0};
+// query tiles ordered by head and K/V-column signature, then XCD runs
+constexpr Org kSplitKSimXcd = {"splitk_sim_xcd", 2, kXcdRun, 2};
 
 std::vector<CatalogEntry> build_catalog() {
   // Kernel tile shapes instantiated for gfx950 (attn_kernels.hip) and the
@@ -63,6 +65,9 @@ std::vector<CatalogEntry> build_catalog() {
       {128, 128, 32, {kSplitK}},
       {64, 32, 256, {kSplitK}},
       {128, 32, 256, {kSplitK}},
+      // signature order (kept last so the ids of the entries above are stable)
+      {128, 32, 128, {kSplitKSimXcd}},
+      {128, 64, 128, {kSplitKSimXcd}},
   };
   std::vector<CatalogEntry> c;
   for (const Shape& sh : shapes) {

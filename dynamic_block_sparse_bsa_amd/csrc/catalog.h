@@ -27,7 +27,8 @@ struct CatalogEntry {
   int split;      // 0: one task per query tile; s >= 1: balance rule with
                   // partitions of at most 2/s of the even share per slot
   int xcd_remap;  // > 0: runs of this many consecutive tasks per XCD
-  int order;      // 0: tasks in query-tile order; 1: longest first
+  int order;      // 0: tasks in query-tile order; 1: longest first; 2: by head
+                  // and K/V-column signature
   std::string name;
 };
 

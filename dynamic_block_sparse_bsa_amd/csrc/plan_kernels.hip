@@ -364,7 +364,8 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
                             int32_t split, int32_t split_min, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
                             int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
                             int32_t dev_split, int32_t slots, int32_t* __restrict__ split_tiles,
-                            unsigned long long stat_nnz, unsigned stat_max_row);
+                            unsigned long long stat_nnz, unsigned stat_max_row,
+                            const int32_t* __restrict__ tcol = nullptr, int32_t ncol = 0);
 
 __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__ mask, int32_t nrows,
                                                      int32_t nkb, int32_t* __restrict__ row_ptr,
@@ -585,13 +586,18 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
 // Traversal order (paper section 3, task organization): order == 0 lists the
 // tasks in query-tile order; order == 1 lists them longest first, so that the
 // in-order dispatch of workgroups approximates a longest-processing-time
-// schedule and the short tasks fill the tail.  Lengths (entries) are counted
-// into kLenBuckets buckets -- exact lengths while max_len < kLenBuckets, else
-// proportional buckets of max_len -- and placed by a counting sort.  Within a
-// bucket, tasks of an earlier 4096-tile chunk of the walk come first; inside
-// a chunk their order follows the LDS atomics.  Every task writes a fixed
-// part of the output (split partials a fixed workspace slot), so the order
-// changes timing, not results.
+// schedule and the short tasks fill the tail; order == 2 lists them by head
+// and, within a head, by a signature of the query tile's K/V columns (the
+// median entry of its tile-list row), so that query tiles that traverse
+// mostly the same K/V tiles -- the rows of one cluster of a clustered mask --
+// are dispatched together (and, with XCD runs, onto one XCD, whose L2 they
+// then share).  Lengths (entries), or (head, signature), are counted into
+// kLenBuckets buckets -- exact lengths while max_len < kLenBuckets, else
+// proportional buckets of max_len; kLenBuckets / H signature buckets per head
+// -- and placed by a counting sort.  Within a bucket, tasks of an earlier
+// 4096-tile chunk of the walk come first; inside a chunk their order follows
+// the LDS atomics.  Every task writes a fixed part of the output (split
+// partials a fixed workspace slot), so the order changes timing, not results.
 constexpr int kLenBuckets = 1024;
 
 struct RowTasks {
@@ -619,6 +625,15 @@ __device__ inline int len_bucket(int len, int max_len) {
   return kLenBuckets - 1 - k;
 }
 
+// Signature bucket of a query tile's row (order == 2): head-major, then the
+// row's median column in bph equal bands of the ncol tile-list columns.
+__device__ inline int sig_bucket(const RowTasks& r, const int32_t* __restrict__ tcol, int ncol, int H) {
+  const int bph = max(1, kLenBuckets / max(H, 1));
+  const int sig = r.e > r.b ? tcol[(r.b + r.e - 1) >> 1] : 0;
+  const int band = min(bph - 1, (int)(((long long)sig * bph) / max(ncol, 1)));
+  return min(kLenBuckets - 1, r.h * bph + band);
+}
+
 __device__ inline Task make_task(const RowTasks& r, int i, int slot0) {
   Task tk;
   tk.head = r.h;
@@ -644,7 +659,8 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
                             int32_t split, int32_t split_min, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
                             int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
                             int32_t dev_split, int32_t slots, int32_t* __restrict__ split_tiles,
-                            unsigned long long stat_nnz, unsigned stat_max_row) {
+                            unsigned long long stat_nnz, unsigned stat_max_row,
+                            const int32_t* __restrict__ tcol, int32_t ncol) {
   __shared__ int32_t lds[32];
   __shared__ int32_t cursor[kLenBuckets];
   const int t = threadIdx.x;
@@ -710,7 +726,8 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
       if (order) {
         for (int i = 0; i < r[k].p; ++i) {
           const Task tk = make_task(r[k], i, off_s);
-          atomicAdd(&cursor[len_bucket(tk.end - tk.begin, max_len)], 1);
+          const int bk = order == 2 ? sig_bucket(r[k], tcol, ncol, H) : len_bucket(tk.end - tk.begin, max_len);
+          atomicAdd(&cursor[bk], 1);
         }
       } else {
         for (int i = 0; i < r[k].p; ++i) tasks[off_t + i] = make_task(r[k], i, off_s);
@@ -758,7 +775,8 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
       if (g0 + k >= nqt) break;
       for (int i = 0; i < r[k].p; ++i) {
         const Task tk = make_task(r[k], i, off_s);
-        tasks[atomicAdd(&cursor[len_bucket(tk.end - tk.begin, max_len)], 1)] = tk;
+        const int bk = order == 2 ? sig_bucket(r[k], tcol, ncol, H) : len_bucket(tk.end - tk.begin, max_len);
+        tasks[atomicAdd(&cursor[bk], 1)] = tk;
       }
       off_s += r[k].p > 1 ? r[k].p : 0;
     }
@@ -774,11 +792,12 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
                                                 int32_t* __restrict__ slot_base,
                                                 Task* __restrict__ tasks, MaskStats* st,
                                                 int32_t dev_split, int32_t slots,
-                                                int32_t* __restrict__ split_tiles) {
+                                                int32_t* __restrict__ split_tiles,
+                                                const int32_t* __restrict__ tcol, int32_t ncol) {
   const unsigned long long nnz = dev_split >= 0 ? st->nnz : 0ull;
   const unsigned max_row = dev_split >= 0 ? st->max_row_nnz : 0u;
   build_tasks(trow_ptr, H, nqt_head, ntr, refine_q, split, split_min, order, max_len, parts, slot_base, tasks,
-              st, dev_split, slots, split_tiles, nnz, max_row);
+              st, dev_split, slots, split_tiles, nnz, max_row, tcol, ncol);
 }
 
 // Stream organization: the concatenated entries of all query tiles (head,
@@ -1027,9 +1046,12 @@ hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_h
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t split_min, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
-                        hipStream_t s, int32_t dev_split, int32_t slots, int32_t* split_tiles) {
+                        hipStream_t s, int32_t dev_split, int32_t slots, int32_t* split_tiles,
+                        const int32_t* tcol, int32_t ncol) {
+  if (order == 2 && !tcol) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tasks, dim3(1), dim3(1024), 0, s, trow_ptr, H, nqt_head, ntr, refine_q, split,
-                     split_min, order, max_len, parts, slot_base, tasks, st, dev_split, slots, split_tiles);
+                     split_min, order, max_len, parts, slot_base, tasks, st, dev_split, slots, split_tiles,
+                     tcol, ncol);
   return hipGetLastError();
 }
 

@@ -21,9 +21,14 @@ not available): clustered top-k masks (per-head densities spread around the
 target, some heads with empty rows), spatiotemporal window masks, i.i.d.
 masks, and i.i.d. masks with one all-active head and one head with empty
 rows, over a range of densities, drawn with seeds disjoint from the
-benchmark's.  Validation uses a float32 masked-attention reference computed
-with torch on the GPU for a sample of rows; a plan whose output deviates by
-more than the parity tolerance on any case is invalid for that case.
+benchmark's.  Validation of every plan on every case: the output is filled
+with NaN before the plan runs and must come back finite everywhere; the rows
+of query blocks without an active block must be exactly zero; every element
+must lie within max|V| (each output row is a convex combination of V rows);
+and sampled rows of every head (16 random rows plus the first and last) must
+match a float32 masked-attention reference computed with torch on the GPU
+within the parity tolerance.  A plan failing any check is invalid for that
+case.
 """
 
 import argparse
@@ -65,7 +70,8 @@ def bucket(bounds, x):
 
 # request keys of the corpus: (B_Q, B_KV), head dim, largest N profiled
 KEYS = [((64, 64), 128, None), ((128, 128), 128, None), ((128, 32), 128, None), ((32, 128), 128, None),
-        ((64, 64), 64, 40960), ((16, 16), 128, 49152), ((32, 16), 128, 49152)]
+        ((64, 64), 64, 40960), ((16, 16), 128, 49152), ((32, 16), 128, 49152),
+        ((64, 64), 32, 75600), ((128, 32), 256, 49152)]
 # two (H, N) sizes in every (head-count bucket, length bucket) cell
 SIZES = [(8, 8192), (4, 12288), (8, 16384), (4, 40960), (4, 75600), (2, 115200),
          (24, 8192), (32, 12288), (24, 16384), (16, 49152), (24, 75600), (16, 115200)]
@@ -166,8 +172,11 @@ def profile(cases, reps=5, warmup=3, log=print, plans=None, save=None, done=()):
         q, k, v = (t.to(dev) for t in gen.qkv(H, N, d, (c["seed"] + 1, c["seed"] + 2, c["seed"] + 3)))
         Md = torch.from_numpy(M).to(dev)
         rng = np.random.default_rng(c["seed"])
-        rows = {h: np.unique(rng.integers(0, N, 48)) for h in range(min(H, 2))}
+        rows = {h: np.unique(np.concatenate([rng.integers(0, N, 16), [0, N - 1]])) for h in range(H)}
         ref = reference_rows(q, k, v, M, (BQ, BKV), rows)
+        # token rows whose query block has no active block: exactly zero
+        empty_tok = (~Md.bool().any(dim=2))[:, torch.arange(N, device=dev) // BQ]
+        vmax = v.abs().amax().float().item()
         out = torch.empty_like(q)
         lat = {}
         stats = None
@@ -184,12 +193,17 @@ def profile(cases, reps=5, warmup=3, log=print, plans=None, save=None, done=()):
             stats = (info["density"], info["run_coverage"], info["row_skew"])
             ts = []
             nw, nr = (1, 3) if H >= 16 else (warmup, reps)  # many-head cases run 10-100 ms
+            out.fill_(float("nan"))
             for i in range(nw + nr):
                 _, a_ms, m_ms = bsa.run_timed(p, q, k, v, out)
                 if i >= nw:
                     ts.append(a_ms + m_ms)
             torch.cuda.synchronize()
-            ok = True
+            ok = bool(torch.isfinite(out).all())
+            if ok and bool(empty_tok.any()):
+                ok = float(out[empty_tok].abs().amax()) == 0.0
+            if ok:
+                ok = float(out.abs().amax()) <= vmax * (1.0 + 1e-2)
             for h, r in rows.items():
                 o = out[h, torch.as_tensor(r, device=dev)].float()
                 err = (o - ref[h]).abs()
@@ -206,7 +220,7 @@ def profile(cases, reps=5, warmup=3, log=print, plans=None, save=None, done=()):
             f"density={rec['density']:.3f} runcov={rec['run_coverage']:.2f} skew={rec['row_skew']:.2f} "
             f"valid={len(lat)} "
             f"best={cat[best]['name'] if best is not None else '-'} {lat.get(best, 0):.3f} ms")
-        del q, k, v, out, Md
+        del q, k, v, out, Md, empty_tok
         torch.cuda.empty_cache()
         if save:
             save(records)

@@ -129,7 +129,9 @@ typedef struct {
   int32_t split;        /* 0 = never split; s >= 1 = balance rule, partitions of
                            at most 2/s of the even share of entries per slot   */
   int32_t xcd_remap;    /* > 0: runs of this many consecutive tasks per XCD      */
-  int32_t order;        /* 0 = query-tile order, 1 = longest task first          */
+  int32_t order;        /* 0 = query-tile order, 1 = longest task first, 2 = by
+                           head, then by the median K/V column of the query
+                           tile's row (tiles sharing K/V dispatched together) */
   char name[48];
 } bsa_catalog_entry;
 

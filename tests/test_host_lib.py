@@ -25,7 +25,7 @@ def test_library_exports_header_symbols():
 
 
 def test_catalog_and_hash():
-    """The native catalog: 37 entries over 15 kernel tile shapes (31 entries
+    """The native catalog: 39 entries over 15 kernel tile shapes (33 entries
     at d = 64 and 128, where the pages' catalogs hold 14-26 entries per
     architecture, plus one per shape at d = 32 and 256), every shape with the
     default organization that base plans use, every entry a distinct
@@ -33,14 +33,15 @@ def test_catalog_and_hash():
     cat = bsa.catalog()
     shapes = {(e["tile_q"], e["tile_kv"], e["d"]) for e in cat}
     orgs = {(e["split"], e["xcd_remap"], e["order"]) for e in cat}
-    assert len(cat) == 37 and len(shapes) == 15
-    assert orgs <= {(2, 0, 0), (0, 0, 0), (2, 16, 0), (2, 128, 0), (2, 0, 1), (3, 0, 1), (4, 0, 1), (0, 0, 1)}
+    assert len(cat) == 39 and len(shapes) == 15
+    assert orgs <= {(2, 0, 0), (0, 0, 0), (2, 16, 0), (2, 128, 0), (2, 0, 1), (3, 0, 1), (4, 0, 1), (0, 0, 1),
+                    (2, 16, 2)}
     for sh in shapes:
         assert any((e["tile_q"], e["tile_kv"], e["d"]) == sh and (e["split"], e["xcd_remap"], e["order"]) == (2, 0, 0)
                    for e in cat), sh
-    assert len({(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"], e["order"]) for e in cat}) == 37
+    assert len({(e["tile_q"], e["tile_kv"], e["d"], e["split"], e["xcd_remap"], e["order"]) for e in cat}) == 39
     per_d = {d: sum(1 for e in cat if e["d"] == d) for d in (32, 64, 128, 256)}
-    assert per_d == {32: 4, 64: 11, 128: 20, 256: 2}
+    assert per_d == {32: 4, 64: 11, 128: 22, 256: 2}
     names = [e["name"] for e in cat]
     assert len(set(names)) == len(names)
     assert re.fullmatch(r"[0-9a-f]{16}", bsa.catalog_hash())
