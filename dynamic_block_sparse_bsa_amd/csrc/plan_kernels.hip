@@ -591,14 +591,17 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
 // median entry of its tile-list row), so that query tiles that traverse
 // mostly the same K/V tiles -- the rows of one cluster of a clustered mask --
 // are dispatched together (and, with XCD runs, onto one XCD, whose L2 they
-// then share).  Lengths (entries), or (head, signature), are counted into
-// kLenBuckets buckets -- exact lengths while max_len < kLenBuckets, else
-// proportional buckets of max_len; kLenBuckets / H signature buckets per head
-// -- and placed by a counting sort.  Within a bucket, tasks of an earlier
+// then share).  Lengths (entries) are counted into kLenBuckets buckets --
+// exact lengths while max_len < kLenBuckets, else proportional buckets of
+// max_len -- or (head, signature) into kSigBuckets buckets (kSigBuckets / H
+// signature bands per head, fine enough that a band holds a handful of
+// neighbouring query tiles of a smoothly varying mask), and placed by a
+// counting sort.  Within a bucket, tasks of an earlier
 // 4096-tile chunk of the walk come first; inside a chunk their order follows
 // the LDS atomics.  Every task writes a fixed part of the output (split
 // partials a fixed workspace slot), so the order changes timing, not results.
 constexpr int kLenBuckets = 1024;
+constexpr int kSigBuckets = 8192;
 
 struct RowTasks {
   int h, qt, b, e, p, chunk;
@@ -628,10 +631,10 @@ __device__ inline int len_bucket(int len, int max_len) {
 // Signature bucket of a query tile's row (order == 2): head-major, then the
 // row's median column in bph equal bands of the ncol tile-list columns.
 __device__ inline int sig_bucket(const RowTasks& r, const int32_t* __restrict__ tcol, int ncol, int H) {
-  const int bph = max(1, kLenBuckets / max(H, 1));
+  const int bph = max(1, kSigBuckets / max(H, 1));
   const int sig = r.e > r.b ? tcol[(r.b + r.e - 1) >> 1] : 0;
   const int band = min(bph - 1, (int)(((long long)sig * bph) / max(ncol, 1)));
-  return min(kLenBuckets - 1, r.h * bph + band);
+  return min(kSigBuckets - 1, r.h * bph + band);
 }
 
 __device__ inline Task make_task(const RowTasks& r, int i, int slot0) {
@@ -662,8 +665,10 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
                             unsigned long long stat_nnz, unsigned stat_max_row,
                             const int32_t* __restrict__ tcol, int32_t ncol) {
   __shared__ int32_t lds[32];
-  __shared__ int32_t cursor[kLenBuckets];
+  __shared__ int32_t cursor[kSigBuckets];
   const int t = threadIdx.x;
+  const int nbk = order == 2 ? kSigBuckets : kLenBuckets;  // buckets in use
+  constexpr int kPer = kSigBuckets / 1024;                 // buckets per thread at most
   const int nqt = H * nqt_head;
   if (dev_split >= 0) {
     const long long W = (long long)refine_q * (long long)stat_nnz;
@@ -681,7 +686,8 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
     max_len = sp > 0 ? (int32_t)sp : (int32_t)min(row_max, (long long)(1 << 30));
   }
   max_len = max(max_len, 1);
-  if (order) cursor[t] = 0;
+  if (order)
+    for (int i = t; i < nbk; i += 1024) cursor[i] = 0;
   __syncthreads();
   // pass 1: partition counts and workspace slots in query-tile order; the
   // tasks themselves (query-tile order) or their length histogram
@@ -745,9 +751,26 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
   if (!order) return;
   // bucket starts, then pass 2 places every task at its bucket's cursor
   __syncthreads();
-  int32_t tot;
-  const int32_t start = block_scan(cursor[t], lds, &tot);
-  cursor[t] = start;
+  {
+    // exclusive scan of the bucket counts: thread t owns buckets
+    // [t * per, (t + 1) * per)
+    const int per = nbk / 1024;
+    int32_t c[kPer];
+    int32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      c[i] = i < per ? cursor[t * per + i] : 0;
+      sum += c[i];
+    }
+    int32_t tot;
+    int32_t run = block_scan(sum, lds, &tot);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (i < per) {
+        cursor[t * per + i] = run;
+        run += c[i];
+      }
+  }
   __syncthreads();
   carry_s = 0;
   for (int base = 0; base < nqt; base += 4096) {

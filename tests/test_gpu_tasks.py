@@ -15,7 +15,7 @@ checked against the organization's definition:
 * query-tile order lists tasks by (head, query tile, begin); longest-first
   order lists the same tasks by non-increasing length; signature order lists
   them by head, and within a head by non-decreasing band of the median column
-  of the query tile's row (kLenBuckets / H bands over the row's columns).
+  of the query tile's row (8192 / H bands over the row's columns).
 
 The masks are large enough (more than 4096 query tiles) that the task
 builder walks several chunks; sampled output rows of each longest-first plan
@@ -115,13 +115,13 @@ def test_task_organizations(block, N, H, min_checked):
             assert (np.diff(ln) <= 0).all(), f"{label}: not longest first"
         if e["order"] == 2:
             nkt = M.shape[2]  # uncoarsened: the tile list is the block-CSR
-            bph = max(1, 1024 // H)
+            bph = max(1, 8192 // H)
             key = []
             for h_, q_ in zip(head.tolist(), qt.tolist()):
                 i = h_ * nqb + q_ // info["refine_q"]
                 b_, e_ = int(rp[i]), int(rp[i + 1])
                 sig = int(cols[(b_ + e_ - 1) // 2]) if e_ > b_ else 0
-                key.append(min(1023, h_ * bph + min(bph - 1, sig * bph // max(nkt, 1))))
+                key.append(min(8191, h_ * bph + min(bph - 1, sig * bph // max(nkt, 1))))
             assert (np.diff(np.array(key)) >= 0).all(), f"{label}: not in signature order"
         # split slots: distinct, consecutive per query tile in partition order
         s = slot[slot >= 0]
