@@ -154,7 +154,8 @@ def cpu_baseline(cfg, budget_s, whole_heads):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; for --config 5 the whole stream, --requests)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--requests", type=int, default=50, help="stream length for --config 5")
@@ -199,6 +200,8 @@ def main():
     # requests: (mask on device, block, flops)
     reqs = []
     nreq = args.requests if args.config == 5 else 1
+    if args.steps is None:
+        args.steps = nreq if args.config == 5 else 20
     for r in range(nreq):
         if args.config == 5:
             BQ, BKV, M, _ = gen.request_c5(r)
