@@ -160,6 +160,24 @@ def qkv(H, N, d, seeds, threads=8, std=(1.0, 1.0, 1.0)):
     return tuple(out)
 
 
+def qkv_device(shape, seeds, device, std=1.0):
+    """bf16 device tensors Q, K, V of the given shape, element ~ N(0, std^2)
+    float32 from torch's generator on `device` seeded per tensor, rounded to
+    bfloat16 (RNE).  For sizes whose host generation would take minutes; the
+    oracle reads the same values back from the device."""
+    import torch
+
+    out = []
+    for s_ in seeds:
+        g = torch.Generator(device=device)
+        g.manual_seed(int(s_))
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        out.append(t.to(torch.bfloat16))
+    return tuple(out)
+
+
 def mask_for(c, r=0):
     """(BQ, BKV, mask) for workload c (request r for the request stream)."""
     cfg = CONFIGS[c]
@@ -208,5 +226,5 @@ def random_case(H, N, d, BQ, BKV, p, seed, empty_rows=None, dense_heads=(), std=
     return M, q, k, v
 
 
-__all__ = ["CONFIGS", "GEOMETRIES_C5", "config", "qkv", "mask_iid_diag",
+__all__ = ["CONFIGS", "GEOMETRIES_C5", "config", "qkv", "qkv_device", "mask_iid_diag",
            "mask_spatiotemporal", "mask_clustered", "request_c5", "random_case", "mask_for"]
