@@ -49,13 +49,16 @@ def heldout(quick=False):
     from dynamic_block_sparse_bsa_amd import profile_table as pt
     cases = []
     seed = 950000
-    keys = [((64, 64), 128), ((128, 128), 128), ((128, 32), 128), ((32, 128), 128), ((16, 16), 128)]
+    # (block, head dim, largest profiled N of the key); keys added later are
+    # appended so the earlier cases keep their seeds
+    keys = [((64, 64), 128, None), ((128, 128), 128, None), ((128, 32), 128, None), ((32, 128), 128, None),
+            ((16, 16), 128, 49152), ((64, 64), 32, 75600), ((128, 32), 256, 49152)]
     sizes = [(8, 8192), (4, 32768), (4, 75600), (24, 75600)] if not quick else [(4, 8192)]
     dens = [0.05, 0.12, 0.22, 0.35] if not quick else [0.15]
     fams = ["clustered", "iid_mixed", "window", "iid"]
-    for block, d in keys:
+    for block, d, nmax in keys:
         for H, N in sizes:
-            if block[1] == 16 and N > 49152:  # the profiled lengths of the 16-token keys
+            if nmax is not None and N > nmax:  # beyond the key's profiled lengths
                 continue
             for i, rho in enumerate(dens):
                 if H >= 16 and i % 2:  # many-head cases: two densities per key

@@ -1,6 +1,6 @@
 """The selection-quality ablation harness on the GPU (Tessera paper, section
 7.4 and Table 7: Direct mapping A0, exhaustive online probing A1, the plan
-table A2), on two held-out cases: the harness runs end to end, its summary
+table A2), on three held-out cases (one at head dim 256): the harness runs end to end, its summary
 is consistent with its rows, and the plan the table selects for each case
 (A2) reproduces the fp64 oracle's output through the library."""
 
@@ -19,10 +19,11 @@ pytestmark = pytest.mark.gpu
 
 def test_quick_ablation_and_selected_plan_against_oracle():
     cases, make_mask = ablation.heldout(quick=True)
-    cases = [cases[0], cases[2]]  # keys (64, 64) and (128, 32)
+    cases = [cases[0], cases[2], cases[6]]  # keys (64, 64) and (128, 32) at d = 128, (128, 32) at d = 256
+    assert (cases[2]["d"], cases[2]["block"]) == (256, (128, 32))
     rows = ablation.run(cases, make_mask, reps=2, warmup=1, log=lambda s: print(s, flush=True))
     s = ablation.summarize(rows)
-    assert s["cases"] == 2
+    assert s["cases"] == 3
     reg = [r["k_a2"] / r["k_best"] for r in rows]
     assert min(reg) >= 1.0 and s["selection_regret"]["max"] == pytest.approx(max(reg))
     assert s["A2_output_vs_reference"]["max_abs_err"] <= 1e-2
