@@ -40,7 +40,7 @@ def tile_cells(p, block, N):
     cq, ckv = min(BQ, TQ), min(BKV, TKV)
     nq, nk = -(-N // cq), -(-N // ckv)
     head, qt, kt, bits = p.export_tiles()
-    cov = np.zeros((p.H, nq, nk), dtype=np.int64)
+    cov = np.zeros((p.H * p.batch, nq, nk), dtype=np.int64)  # every (batch entry, head)
     for a in range(cQ):
         for b in range(cKV):
             sel = ((bits >> np.uint32(a * cKV + b)) & 1).astype(bool)
@@ -66,9 +66,9 @@ def cell_counts_by_head(p, block, N):
     head, qt, kt, bits = p.export_tiles()
     order = np.argsort(head, kind="stable")
     head, qt, kt, bits = head[order], qt[order], kt[order], bits[order]
-    bounds = np.searchsorted(head, np.arange(p.H + 1))
+    bounds = np.searchsorted(head, np.arange(p.H * p.batch + 1))
     assert bounds[-1] == head.size, "tile with a head index out of range"
-    for h in range(p.H):
+    for h in range(p.H * p.batch):
         s, e = bounds[h], bounds[h + 1]
         q_h = qt[s:e].astype(np.int64)
         k_h = kt[s:e].astype(np.int64)
