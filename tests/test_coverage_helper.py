@@ -19,8 +19,9 @@ from bsa_testutil import cell_counts_by_head
 
 
 class FakePlan:
-    def __init__(self, H, info, tiles):
+    def __init__(self, H, info, tiles, batch=1):
         self.H = H
+        self.batch = batch
         self.info = info
         self._tiles = tuple(np.asarray(t) for t in tiles)
 
@@ -110,6 +111,9 @@ def test_expansion_matches_oracle(N, block, T, kind):
     want = coverage.cells(M, BQ, BKV, N, cq, ckv)
     got = _expand(FakePlan(H, info, tiles), block, N)
     assert np.array_equal(got, want)
+    # the same tiles as one head per batch entry: heads are counted over
+    # batch x H, not H alone
+    assert np.array_equal(_expand(FakePlan(1, info, tiles, batch=H), block, N), want)
     # a dropped tile, a duplicated tile and a tile on an inactive block are
     # all detected
     drop = tuple(t[1:] for t in tiles)
