@@ -170,9 +170,10 @@ constexpr bool use_w3() { return TKV == 32 && D == 128 && TQ == 128; }
 // waves per SIMD) fit a CU; uncapped the compiler takes 300 and one fits.
 template <int TQ, int TKV, int D>
 constexpr bool use_w2() { return TKV == 64 && D == 128 && TQ == 128; }
-// K fragments read ahead of their MFMA: deeper where registers allow.
+// K fragments read ahead of their MFMA.  Four fit every variant, the
+// 168-register three-waves-per-SIMD one included; six spill there.
 template <int TQ, int TKV, int D>
-constexpr int kpf_depth() { return use_w3<TQ, TKV, D>() ? 2 : 4; }
+constexpr int kpf_depth() { return 4; }
 
 template <int TQ, int TKV, int D>
 __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
