@@ -6,7 +6,8 @@ Tessera paper, section 5.1 "Offline Plan-Table Compilation":
   1. every profiling case (a mask with its request parameters) is run with
      every eligible catalog plan; each output is validated against a
      masked-attention reference and the median kernel latency L[M, P] of the
-     valid plans is recorded;
+     valid plans is recorded (here in two or more sessions, on separate
+     boxes, combined per case by geometric mean: combine_sessions);
   2. cases are grouped in two stages: by the request key (architecture,
      logical geometry, tensor properties), then by bucketed request
      dimensions and mask statistics (density, active-block-run coverage);
@@ -77,6 +78,31 @@ SIZES = [(8, 8192), (4, 12288), (8, 16384), (4, 40960), (4, 75600), (2, 115200),
          (24, 8192), (32, 12288), (24, 16384), (16, 49152), (24, 75600), (16, 115200)]
 # four target densities in every density bucket
 DENSITIES = [0.03, 0.05, 0.07, 0.09, 0.11, 0.15, 0.19, 0.23, 0.28, 0.35, 0.42, 0.5]
+
+
+def combine_sessions(records):
+    """Records of several profiling sessions (and shards) as one record per
+    case.  Records with the same seed are the same case measured in separate
+    sessions: a plan keeps the geometric mean of its latencies and stays valid
+    only if every session validated it.  Timings of one plan on one case vary
+    by a few percent from box to box, enough to reorder near-equal plans, so
+    rankings rest on every session measured.  Records of distinct seeds (the
+    shards of one session) pass through unchanged; the result is in seed
+    order and records how many sessions each case combines."""
+    by_seed = {}
+    for r in records:
+        by_seed.setdefault(r["seed"], []).append(r)
+    out = []
+    for seed in sorted(by_seed):
+        rs = by_seed[seed]
+        if len(rs) == 1:
+            out.append(dict(rs[0], sessions=rs[0].get("sessions", 1)))
+            continue
+        common = set.intersection(*[set(r["latency"]) for r in rs])
+        lat = {p: math.exp(sum(math.log(r["latency"][p]) for r in rs) / len(rs)) for p in sorted(common)}
+        n = sum(r.get("sessions", 1) for r in rs)
+        out.append(dict(rs[0], latency=lat, sessions=n))
+    return out
 
 
 def corpus(quick=False):
@@ -447,7 +473,8 @@ def main():
     ap.add_argument("--version", default=None)
     ap.add_argument("--records", default=None, help="also write the profiling records (JSON) here")
     ap.add_argument("--from-records", default=None, nargs="+",
-                    help="compile from saved records (no GPU); several files are concatenated")
+                    help="compile from saved records (no GPU); several files are merged by "
+                         "combine_sessions (shards concatenate, sessions of one case combine)")
     ap.add_argument("--shard", default=None, help="i/n: profile every n-th case starting at i")
     ap.add_argument("--plans", default=None, help="profile only catalog entries matching this regex")
     ap.add_argument("--partition", default="auto",
@@ -462,6 +489,10 @@ def main():
         for r in recs:
             r["block"] = tuple(r["block"])
             r["latency"] = {int(k): v for k, v in r["latency"].items()}
+        recs = combine_sessions(recs)
+        if a.records:  # the combined records, as shipped beside the table
+            with open(a.records, "w") as f:
+                json.dump([dict(r, latency={str(k): v for k, v in r["latency"].items()}) for r in recs], f)
     else:
         cases = corpus(a.quick)
         if a.shard:
@@ -493,6 +524,10 @@ def main():
         part = ("tree", int(a.partition.split(":")[1]))
     how = ("compiled from saved records" if a.from_records
            else "profiled and compiled in %.0f s" % (time.time() - t0))
+    ns = sorted({r.get("sessions", 1) for r in recs})
+    if ns != [1]:
+        how += " (%s profiling sessions per case, latencies combined by geometric mean)" % "-".join(
+            str(n) for n in sorted({ns[0], ns[-1]}))
     text = ("# Plan table for gfx950 (MI355X): %d synthetic profiling cases, %s by\n"
             "# profile_table.py.  Format: see csrc/catalog.cpp.\n" % (len(recs), how))
     text += cvtext + compile_table(recs, version, part)

@@ -189,6 +189,23 @@ def test_ablation_plan_cache_repeats():
     assert c["median_check_ms"] == pytest.approx(0.1)  # median of 0.25, 0.05, 0.1
 
 
+def test_sessions_combine_by_geometric_mean():
+    """Records of one case from two sessions become one record: latencies
+    combine by geometric mean, a plan invalid in either session is dropped,
+    and shards of distinct cases pass through in seed order."""
+    a = dict(seed=7, block=(64, 64), latency={1: 1.0, 2: 4.0, 3: 2.0})
+    b = dict(seed=7, block=(64, 64), latency={1: 4.0, 2: 1.0})
+    c = dict(seed=5, block=(64, 64), latency={1: 3.0})
+    out = pt.combine_sessions([a, c, b])
+    assert [r["seed"] for r in out] == [5, 7]
+    assert out[0]["latency"] == {1: 3.0} and out[0]["sessions"] == 1
+    assert out[1]["sessions"] == 2
+    assert set(out[1]["latency"]) == {1, 2}
+    assert out[1]["latency"][1] == pytest.approx(2.0) and out[1]["latency"][2] == pytest.approx(2.0)
+    # already-combined records count their sessions
+    assert pt.combine_sessions([out[1], dict(a)])[0]["sessions"] == 3
+
+
 def test_builtin_table_recompiles_from_its_records():
     """The shipped table is exactly what the compiler makes of the shipped
     profiling records (same catalog, same bounds, same rankings)."""
