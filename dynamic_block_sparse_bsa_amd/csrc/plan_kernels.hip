@@ -360,6 +360,7 @@ __device__ inline uint32_t nz_bits16(const u32x4v x) {
 // stored (and published to the host, sequence number last), and only then
 // are the columns compacted from the bitmap, so the host's plan selection
 // overlaps the compaction.  Same outputs as k_row_count + k_scan + k_compact.
+template <int TPT>
 __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr, int32_t refine_q,
                             int32_t split, int32_t split_min, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
                             int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__
   if (spec.enabled) {
     // the speculative task list, from the row offsets in LDS
     __syncthreads();
-    build_tasks(off, spec.H, spec.nqt_head, spec.ntr, spec.refine_q, 0, 0, spec.order, 0, spec.parts,
+    build_tasks<4>(off, spec.H, spec.nqt_head, spec.ntr, spec.refine_q, 0, 0, spec.order, 0, spec.parts,
                 spec.slot_base, spec.tasks, st, spec.dev_split, spec.slots, spec.split_tiles, s_nnz, s_maxrow);
   }
   // column compaction, one thread per (row, 32-column word): the word's
@@ -596,9 +597,10 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
 // max_len -- or (head, signature) into kSigBuckets buckets (kSigBuckets / H
 // signature bands per head, fine enough that a band holds a handful of
 // neighbouring query tiles of a smoothly varying mask), and placed by a
-// counting sort.  Within a bucket, tasks of an earlier
-// 4096-tile chunk of the walk come first; inside a chunk their order follows
-// the LDS atomics.  Every task writes a fixed part of the output (split
+// counting sort.  Within a bucket, tasks of an earlier chunk of the walk
+// (1024 threads x TPT consecutive tiles) come first; inside a chunk their
+// order follows the LDS atomics (the partitions of one tile that share a
+// bucket stay together).  Every task writes a fixed part of the output (split
 // partials a fixed workspace slot), so the order changes timing, not results.
 constexpr int kLenBuckets = 1024;
 constexpr int kSigBuckets = 8192;
@@ -657,7 +659,9 @@ __device__ inline Task make_task(const RowTasks& r, int i, int slot0) {
 // before the host has read the statistics.
 // The builder runs in one workgroup of 1024 threads: as its own kernel
 // (k_tasks) or inside k_mask_small.  stat_nnz / stat_max_row are the
-// statistics the device split rule reads (dev_split >= 0).
+// statistics the device split rule reads (dev_split >= 0).  TPT: query tiles
+// per thread and chunk of the walk (more tiles in flight, more registers).
+template <int TPT>
 __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr, int32_t refine_q,
                             int32_t split, int32_t split_min, int32_t order, int32_t max_len, int32_t* __restrict__ parts,
                             int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
@@ -666,6 +670,7 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
                             const int32_t* __restrict__ tcol, int32_t ncol) {
   __shared__ int32_t lds[32];
   __shared__ int32_t cursor[kSigBuckets];
+  constexpr int kChunk = 1024 * TPT;  // query tiles per chunk; a thread's TPT loads are issued together
   const int t = threadIdx.x;
   const int nbk = order == 2 ? kSigBuckets : kLenBuckets;  // buckets in use
   constexpr int kPer = kSigBuckets / 1024;                 // buckets per thread at most
@@ -689,52 +694,76 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
   if (order)
     for (int i = t; i < nbk; i += 1024) cursor[i] = 0;
   __syncthreads();
+  // Buckets of a tile's partitions: order 2 puts all of them in the row's
+  // signature bucket; order 1 puts the full-length ones (all but the last) in
+  // their length's bucket and the last, which may be shorter, in its own.
+  // Bucket a takes partitions [0, na), bucket b partition p - 1 when nb = 1.
+  struct Place {
+    int a, na, b, nb;
+  };
+  auto place = [&](const RowTasks& r, int sig) {
+    Place q;
+    if (order == 2) {
+      q.a = sig;
+      q.na = r.p;
+      q.b = 0;
+      q.nb = 0;
+    } else {
+      q.a = len_bucket(r.chunk, max_len);
+      q.na = r.p - 1;
+      q.b = len_bucket((r.e - r.b) - (r.p - 1) * r.chunk, max_len);
+      q.nb = 1;
+    }
+    return q;
+  };
+  // the chunk's rows and, for order 2, their signature buckets (every
+  // signature load in flight before the first is used)
+  auto load_rows = [&](int g0, RowTasks (&r)[TPT], int32_t (&sig)[TPT]) {
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      r[k].p = 0;
+      if (g0 + k < nqt) r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split, split_min);
+    }
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) sig[k] = (order == 2 && g0 + k < nqt) ? sig_bucket(r[k], tcol, ncol, H) : 0;
+  };
   // pass 1: partition counts and workspace slots in query-tile order; the
-  // tasks themselves (query-tile order) or their length histogram
+  // tasks themselves (query-tile order) or their bucket histogram
   int32_t carry_t = 0, carry_s = 0, carry_x = 0;
-  RowTasks keep[4];  // a single chunk's rows and slot offset, reused by pass 2
-  int32_t keep_off_s = 0;
-  for (int base = 0; base < nqt; base += 4096) {
-    const int g0 = base + 4 * t;
-    RowTasks r[4];
+  for (int base = 0; base < nqt; base += kChunk) {
+    const int g0 = base + TPT * t;
+    RowTasks r[TPT];
+    int32_t sig[TPT];
+    load_rows(g0, r, sig);
     int32_t sum_t = 0, sum_s = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      r[k].p = 0;
-      if (g0 + k < nqt) {
-        r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split, split_min);
-        sum_t += r[k].p;
-        sum_s += r[k].p > 1 ? r[k].p : 0;
-      }
+    for (int k = 0; k < TPT; ++k) {
+      sum_t += r[k].p;
+      sum_s += r[k].p > 1 ? r[k].p : 0;
     }
     int32_t tot_t, tot_s;
     int32_t off_t = carry_t + block_scan(sum_t, lds, &tot_t);
     int32_t off_s = carry_s + block_scan(sum_s, lds, &tot_s);
-    keep_off_s = off_s;
     if (split_tiles) {
       int32_t nsp = 0, tot_x;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) nsp += r[k].p > 1;
+      for (int k = 0; k < TPT; ++k) nsp += r[k].p > 1;
       int32_t off_x = carry_x + block_scan(nsp, lds, &tot_x);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < TPT; ++k)
         if (r[k].p > 1) split_tiles[off_x++] = g0 + k;
       carry_x += tot_x;
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) keep[k] = r[k];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < TPT; ++k) {
       const int g = g0 + k;
       if (g >= nqt) break;
       parts[g] = r[k].p;
       slot_base[g] = off_s;
       if (order) {
-        for (int i = 0; i < r[k].p; ++i) {
-          const Task tk = make_task(r[k], i, off_s);
-          const int bk = order == 2 ? sig_bucket(r[k], tcol, ncol, H) : len_bucket(tk.end - tk.begin, max_len);
-          atomicAdd(&cursor[bk], 1);
-        }
+        const Place q = place(r[k], sig[k]);
+        if (q.na) atomicAdd(&cursor[q.a], q.na);
+        if (q.nb) atomicAdd(&cursor[q.b], q.nb);
       } else {
         for (int i = 0; i < r[k].p; ++i) tasks[off_t + i] = make_task(r[k], i, off_s);
       }
@@ -773,34 +802,33 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
   }
   __syncthreads();
   carry_s = 0;
-  for (int base = 0; base < nqt; base += 4096) {
-    const int g0 = base + 4 * t;
-    RowTasks r[4];
-    int32_t off_s, tot_s = 0;
-    if (nqt <= 4096) {  // one chunk: its rows are still in registers
+  for (int base = 0; base < nqt; base += kChunk) {
+    const int g0 = base + TPT * t;
+    RowTasks r[TPT];
+    int32_t sig[TPT];
+    int32_t tot_s;
+    load_rows(g0, r, sig);  // again: holding every chunk's rows would spill
+    int32_t sum_s = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) r[k] = keep[k];
-      off_s = keep_off_s;
-    } else {
-      int32_t sum_s = 0;
+    for (int k = 0; k < TPT; ++k) sum_s += r[k].p > 1 ? r[k].p : 0;
+    int32_t off_s = carry_s + block_scan(sum_s, lds, &tot_s);
+    // claim every tile's places first (independent atomics), then write
+    int32_t pa[TPT], pb[TPT];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        r[k].p = 0;
-        if (g0 + k < nqt) {
-          r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split, split_min);
-          sum_s += r[k].p > 1 ? r[k].p : 0;
-        }
+    for (int k = 0; k < TPT; ++k) {
+      pa[k] = pb[k] = 0;
+      if (g0 + k < nqt) {
+        const Place q = place(r[k], sig[k]);
+        if (q.na) pa[k] = atomicAdd(&cursor[q.a], q.na);
+        if (q.nb) pb[k] = atomicAdd(&cursor[q.b], q.nb);
       }
-      off_s = carry_s + block_scan(sum_s, lds, &tot_s);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < TPT; ++k) {
       if (g0 + k >= nqt) break;
-      for (int i = 0; i < r[k].p; ++i) {
-        const Task tk = make_task(r[k], i, off_s);
-        const int bk = order == 2 ? sig_bucket(r[k], tcol, ncol, H) : len_bucket(tk.end - tk.begin, max_len);
-        tasks[atomicAdd(&cursor[bk], 1)] = tk;
-      }
+      const Place q = place(r[k], sig[k]);
+      for (int i = 0; i < q.na; ++i) tasks[pa[k] + i] = make_task(r[k], i, off_s);
+      if (q.nb) tasks[pb[k]] = make_task(r[k], r[k].p - 1, off_s);
       off_s += r[k].p > 1 ? r[k].p : 0;
     }
     carry_s += tot_s;
@@ -819,7 +847,7 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
                                                 const int32_t* __restrict__ tcol, int32_t ncol) {
   const unsigned long long nnz = dev_split >= 0 ? st->nnz : 0ull;
   const unsigned max_row = dev_split >= 0 ? st->max_row_nnz : 0u;
-  build_tasks(trow_ptr, H, nqt_head, ntr, refine_q, split, split_min, order, max_len, parts, slot_base, tasks,
+  build_tasks<8>(trow_ptr, H, nqt_head, ntr, refine_q, split, split_min, order, max_len, parts, slot_base, tasks,
               st, dev_split, slots, split_tiles, nnz, max_row, tcol, ncol);
 }
 
