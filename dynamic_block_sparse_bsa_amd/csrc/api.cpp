@@ -322,10 +322,11 @@ struct bsa_plan {
   bool coarse = false;
   MaskStats stats{};
   bsa_plan_info info{};
-  DevBuf stats_dev, row_cnt, row_ptr, row_part, cols, trow_cnt, trow_ptr_buf, tcol_buf, tbits_buf, parts,
-      slot_off, tasks, ws, seg_ptr, spec_parts, spec_slot, spec_tasks, split_tiles, spec_split;
+  DevBuf stats_dev, row_cnt, row_ptr, row_part, cols, rsig, trow_cnt, trow_ptr_buf, tcol_buf, tbits_buf, tsig_buf,
+      parts, slot_off, tasks, ws, seg_ptr, spec_parts, spec_slot, spec_tasks, split_tiles, spec_split;
   const int32_t* trow_ptr = nullptr;
   const int32_t* tcol = nullptr;
+  const int32_t* tsig = nullptr;  // per tile-list row: the column of its median entry
   const uint32_t* tbits = nullptr;
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};  // timing events of bsa_run_timed
   hipEvent_t done = nullptr;  // recorded after plan creation and after untimed runs
@@ -336,8 +337,9 @@ struct bsa_plan {
   }
 
   ~bsa_plan() {
-    for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &row_part, &cols, &trow_cnt, &trow_ptr_buf, &tcol_buf,
-                      &tbits_buf, &parts, &slot_off, &tasks, &ws, &seg_ptr, &spec_parts, &spec_slot, &spec_tasks, &split_tiles, &spec_split})
+    for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &row_part, &cols, &rsig, &trow_cnt, &trow_ptr_buf, &tcol_buf,
+                      &tbits_buf, &tsig_buf, &parts, &slot_off, &tasks, &ws, &seg_ptr, &spec_parts, &spec_slot,
+                      &spec_tasks, &split_tiles, &spec_split})
       pool_release(b);
     for (auto& e : ev) event_put(dev, true, e);
     event_put(dev, false, done);
@@ -698,7 +700,7 @@ static size_t plan_bytes(const CatalogEntry& e, const bsa_request& r, const Plan
   size_t b = 0;
   if (sh.mq.coarsen > 1 || sh.mk.coarsen > 1) {
     const size_t ntrows = (size_t)r.H * (size_t)cdiv(nqb, sh.mq.coarsen);
-    b += arena_size(sizeof(int32_t) * ntrows) + arena_size(sizeof(int32_t) * (ntrows + 1)) +
+    b += 2 * arena_size(sizeof(int32_t) * ntrows) + arena_size(sizeof(int32_t) * (ntrows + 1)) +
          arena_size(sizeof(int32_t) * nnz) + arena_size(sizeof(uint32_t) * nnz);
   }
   b += 2 * arena_size(sizeof(int32_t) * nqt) + arena_size(sizeof(Task) * (size_t)std::max<int64_t>(sh.tasks_upper, 1));
@@ -746,7 +748,7 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
   MaskStats* host = nullptr;
   if (arena) {
     // the mask state's own buffers must fit before anything is launched
-    const size_t need = arena_size(sizeof(MaskStats)) + arena_size(sizeof(int32_t) * ((size_t)nrows + 1)) +
+    const size_t need = arena_size(sizeof(MaskStats)) + 2 * arena_size(sizeof(int32_t) * ((size_t)nrows + 1)) +
                         (mask_small_ok(r.mask, nrows, p->nkb)
                              ? arena_size(sizeof(int32_t) * (size_t)nrows * (size_t)p->nkb)
                              : arena_size(sizeof(int32_t) * (size_t)nrows) +
@@ -760,6 +762,7 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
   }
   HIP_TRY(p->alloc(sizeof(MaskStats), &p->stats_dev));
   HIP_TRY(p->alloc(sizeof(int32_t) * ((size_t)nrows + 1), &p->row_ptr));
+  HIP_TRY(p->alloc(sizeof(int32_t) * ((size_t)nrows + 1), &p->rsig));
   MaskStats* dst = (MaskStats*)p->stats_dev.ptr;
   // speculative task list of the entry this request key selected last time
   // (not with the static scratch: its space goes to the selected plan)
@@ -812,8 +815,8 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
     // (with a prediction, the same kernel also builds the speculative list)
     TaskSpec ts;
     HIP_TRY(prepare_spec(ts));
-    HIP_TRY(launch_mask_small(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, dst, host,
-                              seq, s, ts));
+    HIP_TRY(launch_mask_small(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr,
+                              (int32_t*)p->rsig.ptr, dst, host, seq, s, ts));
     spec_launched = ts.enabled != 0;
   } else {
     HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)nrows, &p->row_cnt));
@@ -837,7 +840,8 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
     early_compact = !arena && cols_bound <= kEarlyCompactBytes;
     if (early_compact) {
       HIP_TRY(p->alloc(cols_bound, &p->cols));
-      HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
+      HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr,
+                             (int32_t*)p->rsig.ptr, s));
     }
   }
   // Wait for the statistics alone (the compaction may still run): spin on the
@@ -901,7 +905,8 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
   const size_t nnz = (size_t)p->stats.nnz;
   if (!early_compact) {
     HIP_TRY(p->alloc(sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->cols));
-    HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, s));
+    HIP_TRY(launch_compact(r.mask, nrows, p->nkb, (int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr,
+                           (int32_t*)p->rsig.ptr, s));
   }
 
   // ---- launch preparation: tile list of the selected mapping -------------------
@@ -915,21 +920,24 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
     HIP_TRY(p->alloc(sizeof(int32_t) * ((size_t)ntrows + 1), &p->trow_ptr_buf));
     HIP_TRY(p->alloc(sizeof(int32_t) * std::max<size_t>(nnz, 1), &p->tcol_buf));
     HIP_TRY(p->alloc(sizeof(uint32_t) * std::max<size_t>(nnz, 1), &p->tbits_buf));
+    HIP_TRY(p->alloc(sizeof(int32_t) * (size_t)ntrows, &p->tsig_buf));
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
-                           ntc, (int32_t*)p->trow_cnt.ptr, nullptr, nullptr, nullptr, s));
+                           ntc, (int32_t*)p->trow_cnt.ptr, nullptr, nullptr, nullptr, nullptr, s));
     HIP_TRY(launch_scan((int32_t*)p->trow_cnt.ptr, (int32_t*)p->trow_ptr_buf.ptr, ntrows, nullptr, 0, nullptr,
                         nullptr, 0, s));
     HIP_TRY(launch_coarsen((int32_t*)p->row_ptr.ptr, (int32_t*)p->cols.ptr, r.H, p->nqb, p->nkb, cq, ckv, p->ntr,
                            ntc, nullptr, (int32_t*)p->trow_ptr_buf.ptr, (int32_t*)p->tcol_buf.ptr,
-                           (uint32_t*)p->tbits_buf.ptr, s));
+                           (uint32_t*)p->tbits_buf.ptr, (int32_t*)p->tsig_buf.ptr, s));
     p->trow_ptr = (const int32_t*)p->trow_ptr_buf.ptr;
     p->tcol = (const int32_t*)p->tcol_buf.ptr;
     p->tbits = (const uint32_t*)p->tbits_buf.ptr;
+    p->tsig = (const int32_t*)p->tsig_buf.ptr;
   } else {
     p->ntr = p->nqb;
     p->trow_ptr = (const int32_t*)p->row_ptr.ptr;
     p->tcol = (const int32_t*)p->cols.ptr;
     p->tbits = nullptr;
+    p->tsig = (const int32_t*)p->rsig.ptr;
   }
 
   // ---- tasks and split-K partitions -----------------------------------------
@@ -960,7 +968,7 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
     HIP_TRY(launch_tasks(p->trow_ptr, r.H, shape.nqt_head, p->ntr, shape.mq.refine, shape.split, shape.split_min,
                          chosen->order,
                          (int32_t)max_len, (int32_t*)p->parts.ptr, (int32_t*)p->slot_off.ptr,
-                         (Task*)p->tasks.ptr, dst, s, -1, 0, (int32_t*)p->split_tiles.ptr, p->tcol,
+                         (Task*)p->tasks.ptr, dst, s, -1, 0, (int32_t*)p->split_tiles.ptr, p->tsig,
                          (int32_t)cdiv(p->nkb, ckv)));
   }
   if (!arena) pred_store(pkey, predictable(*chosen, r) && shape.groups == 0 ? chosen->id : -1);

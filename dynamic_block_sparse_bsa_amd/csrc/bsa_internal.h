@@ -157,15 +157,20 @@ constexpr int kSmallMaskCols = 256;
 bool mask_small_ok(const uint8_t* mask, int32_t nrows, int32_t nkb);
 // spec.enabled: the kernel also builds that task list, right after the
 // statistics are published and before the compaction.
+// The compaction (k_mask_small, k_compact*) also stores, per block-CSR row,
+// the column of its median entry (row_ptr[r] + row_ptr[r + 1] - 1) / 2 into
+// rsig[r] (rows without entries are left unwritten), and the coarsening's
+// write pass does the same per tile row into tsig: the traversal signature
+// of the signature order.
 hipError_t launch_mask_small(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_ptr, int32_t* cols,
-                             MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s,
+                             int32_t* rsig, MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s,
                              const TaskSpec& spec);
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
-                          int32_t* cols, hipStream_t s);
+                          int32_t* cols, int32_t* rsig, hipStream_t s);
 hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,
                           int32_t nkb, int32_t cq, int32_t ckv, int32_t ntr, int32_t ntc,
                           int32_t* trow_cnt, const int32_t* trow_ptr, int32_t* tcol,
-                          uint32_t* tbits, hipStream_t s);
+                          uint32_t* tbits, int32_t* tsig, hipStream_t s);
 // A query tile's row of n > split_min entries is cut into ceil(n / split)
 // partitions.  dev_split >= 0: split, split_min and max_len are derived on
 // the device from *st (the balance rule with split share dev_split in halves
@@ -175,13 +180,14 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
 // The balance rule leaves rows of up to kSplitRowFactor times the mean row
 // length whole: cutting rows of an even mask only adds partials to merge.
 // order: 0 query-tile order, 1 longest first, 2 by head and column signature
-// (needs the tile list's columns tcol and their count ncol).
+// (needs each tile row's median column tsig and the tile-list column count
+// ncol).
 constexpr int kSplitRowFactor = 2;
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t split_min, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
                         hipStream_t s, int32_t dev_split = -1, int32_t slots = 0,
-                        int32_t* split_tiles = nullptr, const int32_t* tcol = nullptr, int32_t ncol = 0);
+                        int32_t* split_tiles = nullptr, const int32_t* tsig = nullptr, int32_t ncol = 0);
 // With a.split_tiles, grid_items (> 0) workgroups loop over the listed
 // (tile, column group) items; otherwise one workgroup per (query tile,
 // column group).  A column group is kMergeCols output columns.

@@ -210,17 +210,22 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in,
 // One wave per query-block row: write the active column indices, ascending.
 __global__ __launch_bounds__(256) void k_compact(const uint8_t* __restrict__ mask, int32_t nrows,
                                                  int32_t nkb, const int32_t* __restrict__ row_ptr,
-                                                 int32_t* __restrict__ cols) {
+                                                 int32_t* __restrict__ cols, int32_t* __restrict__ rsig) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wave >= nrows) return;
   const unsigned l = lane_id();
   const uint8_t* row = mask + (size_t)wave * nkb;
   int32_t out = row_ptr[wave];
+  const int32_t mid = (out + row_ptr[wave + 1] - 1) >> 1;  // the row's median entry
   for (int base = 0; base < nkb; base += 64) {
     const int p = base + (int)l;
     const bool a = p < nkb && row[p] != 0;
     const unsigned long long ba = __ballot(a);
-    if (a) cols[out + (int)prefix_count(ba)] = p;
+    if (a) {
+      const int32_t o = out + (int)prefix_count(ba);
+      cols[o] = p;
+      if (o == mid) rsig[wave] = p;
+    }
     out += __popcll(ba);
   }
 }
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(256) void k_row_count16(const uint8_t* __restrict__
 // counts.
 __global__ __launch_bounds__(256) void k_compact16(const uint8_t* __restrict__ mask, int32_t nrows,
                                                    int32_t nkb, const int32_t* __restrict__ row_ptr,
-                                                   int32_t* __restrict__ cols) {
+                                                   int32_t* __restrict__ cols, int32_t* __restrict__ rsig) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= nrows) return;
   const int l = (int)lane_id();
@@ -326,6 +331,7 @@ __global__ __launch_bounds__(256) void k_compact16(const uint8_t* __restrict__ m
   const size_t a0 = start & ~(size_t)15;
   const int nwin = (int)((start + nkb - a0 + 1023) / 1024);
   int32_t out = row_ptr[row];
+  const int32_t mid = (out + row_ptr[row + 1] - 1) >> 1;  // the row's median entry
   for (int w = 0; w < nwin; ++w) {
     uint32_t m = row_chunk_bits(mask, total, start, nkb, a0, w, l);
     const int32_t c = (int32_t)__popc(m);
@@ -333,7 +339,9 @@ __global__ __launch_bounds__(256) void k_compact16(const uint8_t* __restrict__ m
     int32_t o = out + incl - c;
     const int32_t base = (int32_t)(a0 + (size_t)w * 1024 + 16 * (size_t)l - start);  // column of bit 0
     while (m) {
-      cols[o++] = base + __ffs(m) - 1;
+      const int32_t col = base + __ffs(m) - 1;
+      if (o == mid) rsig[row] = col;
+      cols[o++] = col;
       m &= m - 1u;
     }
     out += __shfl(incl, 63, 64);
@@ -366,12 +374,12 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
                             int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
                             int32_t dev_split, int32_t slots, int32_t* __restrict__ split_tiles,
                             unsigned long long stat_nnz, unsigned stat_max_row,
-                            const int32_t* __restrict__ tcol = nullptr, int32_t ncol = 0);
+                            const int32_t* __restrict__ tsig = nullptr, int32_t ncol = 0);
 
 __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__ mask, int32_t nrows,
                                                      int32_t nkb, int32_t* __restrict__ row_ptr,
-                                                     int32_t* __restrict__ cols, MaskStats* st,
-                                                     MaskStats* host_st, unsigned long long seq,
+                                                     int32_t* __restrict__ cols, int32_t* __restrict__ rsig,
+                                                     MaskStats* st, MaskStats* host_st, unsigned long long seq,
                                                      const TaskSpec spec) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __shared__ uint32_t bits[kSmallMaskBytes / 32 + 1];  // + a zero word read past the last row
@@ -489,11 +497,14 @@ __global__ __launch_bounds__(1024) void k_mask_small(const uint8_t* __restrict__
   __syncthreads();
   for (int it = t; it < nrows * nw; it += 1024) {
     const int r = it / nw, k = it - r * nw;
+    const int32_t mid = (off[r] + off[r + 1] - 1) >> 1;  // the row's median entry
     int32_t o = off[r];
     for (int kk = 0; kk < k; ++kk) o += (int32_t)__popc(row_word(r, kk));
     uint32_t v = row_word(r, k);
     while (v) {
-      cols[o++] = (k << 5) + __ffs(v) - 1;
+      const int32_t c = (k << 5) + __ffs(v) - 1;
+      if (o == mid) rsig[r] = c;
+      cols[o++] = c;
       v &= v - 1u;
     }
   }
@@ -515,7 +526,8 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
                                                  int32_t ntc, int32_t* __restrict__ trow_cnt,
                                                  const int32_t* __restrict__ trow_ptr,
                                                  int32_t* __restrict__ tcol,
-                                                 uint32_t* __restrict__ tbits) {
+                                                 uint32_t* __restrict__ tbits,
+                                                 int32_t* __restrict__ tsig) {
   __shared__ uint32_t bitmap[kCoarsenWin];
   __shared__ int32_t wave_tot[4];
   const int g = blockIdx.x;  // h * ntr + tr
@@ -525,6 +537,7 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
   const int w = threadIdx.x >> 6;
   int cnt = 0;                                   // count pass: this thread's share
   int32_t out = trow_ptr ? trow_ptr[g] : 0;      // write pass: next entry
+  const int32_t mid = trow_ptr ? (out + trow_ptr[g + 1] - 1) >> 1 : -1;  // the row's median entry
   for (int w0 = 0; w0 < ntc; w0 += kCoarsenWin) {
     const int wn = min(kCoarsenWin, ntc - w0);
     for (int i = threadIdx.x; i < wn; i += 256) bitmap[i] = 0u;
@@ -558,6 +571,7 @@ __global__ __launch_bounds__(256) void k_coarsen(const int32_t* __restrict__ row
           const int pos = out + before + (int)prefix_count(bal);
           tcol[pos] = w0 + i;
           tbits[pos] = bits;
+          if (pos == mid) tsig[g] = w0 + i;
         }
         out += total;
         __syncthreads();
@@ -631,10 +645,11 @@ __device__ inline int len_bucket(int len, int max_len) {
 }
 
 // Signature bucket of a query tile's row (order == 2): head-major, then the
-// row's median column in bph equal bands of the ncol tile-list columns.
-__device__ inline int sig_bucket(const RowTasks& r, const int32_t* __restrict__ tcol, int ncol, int H) {
+// row's median column sig (its entry (b + e - 1) / 2, which the compaction or
+// the coarsening stored per row) in bph equal bands of the ncol tile-list
+// columns.
+__device__ inline int sig_bucket(const RowTasks& r, int sig, int ncol, int H) {
   const int bph = max(1, kSigBuckets / max(H, 1));
-  const int sig = r.e > r.b ? tcol[(r.b + r.e - 1) >> 1] : 0;
   const int band = min(bph - 1, (int)(((long long)sig * bph) / max(ncol, 1)));
   return min(kSigBuckets - 1, r.h * bph + band);
 }
@@ -667,7 +682,7 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
                             int32_t* __restrict__ slot_base, Task* __restrict__ tasks, MaskStats* st,
                             int32_t dev_split, int32_t slots, int32_t* __restrict__ split_tiles,
                             unsigned long long stat_nnz, unsigned stat_max_row,
-                            const int32_t* __restrict__ tcol, int32_t ncol) {
+                            const int32_t* __restrict__ tsig, int32_t ncol) {
   __shared__ int32_t lds[32];
   __shared__ int32_t cursor[kSigBuckets];
   constexpr int kChunk = 1024 * TPT;  // query tiles per chunk; a thread's TPT loads are issued together
@@ -716,8 +731,7 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
     }
     return q;
   };
-  // the chunk's rows and, for order 2, their signature buckets (every
-  // signature load in flight before the first is used)
+  // the chunk's rows and, for order 2, their signature buckets
   auto load_rows = [&](int g0, RowTasks (&r)[TPT], int32_t (&sig)[TPT]) {
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
@@ -725,7 +739,10 @@ __device__ __forceinline__ void build_tasks(const int32_t* trow_ptr, int32_t H, 
       if (g0 + k < nqt) r[k] = row_tasks(trow_ptr, g0 + k, nqt_head, ntr, refine_q, split, split_min);
     }
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) sig[k] = (order == 2 && g0 + k < nqt) ? sig_bucket(r[k], tcol, ncol, H) : 0;
+    for (int k = 0; k < TPT; ++k)
+      sig[k] = (order == 2 && g0 + k < nqt)
+                   ? sig_bucket(r[k], r[k].e > r[k].b ? tsig[r[k].h * ntr + r[k].qt / refine_q] : 0, ncol, H)
+                   : 0;
   };
   // pass 1: partition counts and workspace slots in query-tile order; the
   // tasks themselves (query-tile order) or their bucket histogram
@@ -844,11 +861,11 @@ __global__ __launch_bounds__(1024) void k_tasks(const int32_t* __restrict__ trow
                                                 Task* __restrict__ tasks, MaskStats* st,
                                                 int32_t dev_split, int32_t slots,
                                                 int32_t* __restrict__ split_tiles,
-                                                const int32_t* __restrict__ tcol, int32_t ncol) {
+                                                const int32_t* __restrict__ tsig, int32_t ncol) {
   const unsigned long long nnz = dev_split >= 0 ? st->nnz : 0ull;
   const unsigned max_row = dev_split >= 0 ? st->max_row_nnz : 0u;
   build_tasks<8>(trow_ptr, H, nqt_head, ntr, refine_q, split, split_min, order, max_len, parts, slot_base, tasks,
-              st, dev_split, slots, split_tiles, nnz, max_row, tcol, ncol);
+              st, dev_split, slots, split_tiles, nnz, max_row, tsig, ncol);
 }
 
 // Stream organization: the concatenated entries of all query tiles (head,
@@ -1057,31 +1074,34 @@ bool mask_small_ok(const uint8_t* mask, int32_t nrows, int32_t nkb) {
 }
 
 hipError_t launch_mask_small(const uint8_t* mask, int32_t nrows, int32_t nkb, int32_t* row_ptr, int32_t* cols,
-                             MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s,
+                             int32_t* rsig, MaskStats* st, MaskStats* host_st, unsigned long long seq, hipStream_t s,
                              const TaskSpec& spec) {
-  if (!mask_small_ok(mask, nrows, nkb)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_mask_small, dim3(1), dim3(1024), 0, s, mask, nrows, nkb, row_ptr, cols, st, host_st,
+  if (!mask_small_ok(mask, nrows, nkb) || !rsig) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mask_small, dim3(1), dim3(1024), 0, s, mask, nrows, nkb, row_ptr, cols, rsig, st, host_st,
                      seq, spec);
   return hipGetLastError();
 }
 
 hipError_t launch_compact(const uint8_t* mask, int32_t nrows, int32_t nkb, const int32_t* row_ptr,
-                          int32_t* cols, hipStream_t s) {
+                          int32_t* cols, int32_t* rsig, hipStream_t s) {
+  if (!rsig) return hipErrorInvalidValue;
   if (((uintptr_t)mask & 15) == 0)
-    hipLaunchKernelGGL(k_compact16, dim3((nrows + 3) / 4), dim3(256), 0, s, mask, nrows, nkb, row_ptr, cols);
+    hipLaunchKernelGGL(k_compact16, dim3((nrows + 3) / 4), dim3(256), 0, s, mask, nrows, nkb, row_ptr, cols,
+                       rsig);
   else
     hipLaunchKernelGGL(k_compact, dim3((nrows + 3) / 4), dim3(256), 0, s, mask, nrows, nkb, row_ptr,
-                       cols);
+                       cols, rsig);
   return hipGetLastError();
 }
 
 hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H, int32_t nqb,
                           int32_t nkb, int32_t cq, int32_t ckv, int32_t ntr, int32_t ntc,
                           int32_t* trow_cnt, const int32_t* trow_ptr, int32_t* tcol,
-                          uint32_t* tbits, hipStream_t s) {
+                          uint32_t* tbits, int32_t* tsig, hipStream_t s) {
   (void)nkb;
+  if (trow_ptr && !tsig) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_coarsen, dim3(H * ntr), dim3(256), 0, s, row_ptr, cols, nqb, cq, ckv, ntr, ntc, trow_cnt,
-                     trow_ptr, tcol, tbits);
+                     trow_ptr, tcol, tbits, tsig);
   return hipGetLastError();
 }
 
@@ -1098,11 +1118,11 @@ hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, in
                         int32_t refine_q, int32_t split, int32_t split_min, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
                         hipStream_t s, int32_t dev_split, int32_t slots, int32_t* split_tiles,
-                        const int32_t* tcol, int32_t ncol) {
-  if (order == 2 && !tcol) return hipErrorInvalidValue;
+                        const int32_t* tsig, int32_t ncol) {
+  if (order == 2 && !tsig) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tasks, dim3(1), dim3(1024), 0, s, trow_ptr, H, nqt_head, ntr, refine_q, split,
                      split_min, order, max_len, parts, slot_base, tasks, st, dev_split, slots, split_tiles,
-                     tcol, ncol);
+                     tsig, ncol);
   return hipGetLastError();
 }
 
