@@ -149,7 +149,12 @@ hipError_t arena_alloc(Arena* a, int dev, size_t bytes, DevBuf* b) {
 // 256-byte aligned size of a buffer carved from the arena
 size_t arena_size(size_t bytes) { return ((bytes ? bytes : 1) + 255) & ~size_t(255); }
 
-constexpr size_t kEarlyCompactBytes = size_t(16) << 20;
+// Largest column array (sized for every mask block) that is allocated before
+// the statistics are known, so that the compaction can be queued ahead of the
+// host's selection and overlap it.  1 GiB covers masks of 2.7e8 blocks (the
+// largest benchmark masks need 0.2-0.3 GB); the array comes from the device
+// memory cache and holds only the active blocks' columns.
+constexpr size_t kEarlyCompactBytes = size_t(1) << 30;
 
 // Fine-grained (coherent) pinned host memory, one per thread, that the mask
 // state kernels write the statistics into directly: the single device-to-host
