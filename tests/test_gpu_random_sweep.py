@@ -27,7 +27,7 @@ from bsa_testutil import assert_close, tile_cells
 
 pytestmark = pytest.mark.gpu
 
-NCASES = 96
+NCASES = 400
 SPLITS = (-1, 0, 1, 2, 5, bsa.SPLIT_STREAM)
 
 
