@@ -328,7 +328,7 @@ struct bsa_plan {
   MaskStats stats{};
   bsa_plan_info info{};
   DevBuf stats_dev, row_cnt, row_ptr, row_part, cols, rsig, trow_cnt, trow_ptr_buf, tcol_buf, tbits_buf, tsig_buf,
-      parts, slot_off, tasks, ws, seg_ptr, spec_parts, spec_slot, spec_tasks, split_tiles, spec_split;
+      parts, slot_off, tasks, ws, seg_ptr, spec_parts, spec_slot, spec_tasks, split_tiles, spec_split, xq;
   const int32_t* trow_ptr = nullptr;
   const int32_t* tcol = nullptr;
   const int32_t* tsig = nullptr;  // per tile-list row: the column of its median entry
@@ -344,7 +344,7 @@ struct bsa_plan {
   ~bsa_plan() {
     for (DevBuf* b : {&stats_dev, &row_cnt, &row_ptr, &row_part, &cols, &rsig, &trow_cnt, &trow_ptr_buf, &tcol_buf,
                       &tbits_buf, &tsig_buf, &parts, &slot_off, &tasks, &ws, &seg_ptr, &spec_parts, &spec_slot,
-                      &spec_tasks, &split_tiles, &spec_split})
+                      &spec_tasks, &split_tiles, &spec_split, &xq})
       pool_release(b);
     for (auto& e : ev) event_put(dev, true, e);
     event_put(dev, false, done);
@@ -698,7 +698,6 @@ bsa_status bsa_base_plan(const bsa_request* req, int32_t* plan_id) {
 // list, split bookkeeping, split-K workspace), each rounded as the arena does.
 static size_t plan_bytes(const CatalogEntry& e, const bsa_request& r, const PlanShape& sh, const MaskStats& st,
                          int nqb, int nkb) {
-  (void)e;
   (void)nkb;
   const size_t nnz = std::max<size_t>((size_t)st.nnz, 1);
   const size_t nqt = (size_t)sh.nqt;
@@ -712,6 +711,7 @@ static size_t plan_bytes(const CatalogEntry& e, const bsa_request& r, const Plan
   if (sh.groups > 0) b += arena_size(sizeof(int32_t) * (size_t)(sh.groups + 1));
   else if (sh.split > 0) b += arena_size(sizeof(int32_t) * nqt);
   if (sh.slots_upper > 0) b += arena_size((size_t)sh.ws_bytes);
+  if (sh.groups == 0 && e.xcd_remap > 0) b += arena_size(8 * sizeof(unsigned long long));  // XCD queues
   return b;
 }
 
@@ -978,8 +978,13 @@ static bsa_status plan_create_impl(const bsa_request* req, hipStream_t s, std::u
   }
   if (!arena) pred_store(pkey, predictable(*chosen, r) && shape.groups == 0 ? chosen->id : -1);
   if (shape.slots_upper > 0) HIP_TRY(p->alloc((size_t)shape.ws_bytes, &p->ws));
-  const int64_t gran = chosen->xcd_remap > 0 && shape.groups == 0 ? 8 * (int64_t)chosen->xcd_remap : 1;
-  p->grid = shape.groups > 0 ? shape.groups : cdiv(std::max<int64_t>(shape.tasks_upper, 1), gran) * gran;
+  const bool queues = chosen->xcd_remap > 0 && shape.groups == 0;
+  const int64_t gran = queues ? 8 * (int64_t)chosen->xcd_remap : 1;
+  // per-XCD queues: spare workgroups for the fast XCDs to steal with
+  const int64_t spare = queues ? cdiv(std::max<int64_t>(shape.tasks_upper, 1), kXcdSpareDiv) : 0;
+  p->grid = shape.groups > 0 ? shape.groups
+                             : cdiv(std::max<int64_t>(shape.tasks_upper, 1) + spare, gran) * gran;
+  if (queues) HIP_TRY(p->alloc(8 * sizeof(unsigned long long), &p->xq));
   if (p->grid >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many tasks");
   HIP_TRY(hipGetLastError());
 
@@ -1081,10 +1086,12 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   a.coarsen_q = p->shape.mq.coarsen;
   a.bq = r.block_q;
   a.xcd_remap = p->shape.groups > 0 ? 0 : e.xcd_remap;
+  a.xq = a.xcd_remap > 0 ? (unsigned long long*)p->xq.ptr : nullptr;
   a.seg_ptr = p->shape.groups > 0 ? (const int32_t*)p->seg_ptr.ptr : nullptr;
   a.grid = (int32_t)p->grid;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)r.d));
   bsa_plan* mp = const_cast<bsa_plan*>(p);
+  if (a.xq) HIP_TRY(launch_xq_init(a.xq, a.n_tasks, a.xcd_remap, s));
   if (timed) {
     for (auto& ev : mp->ev)
       if (!ev) HIP_TRY(event_get(p->dev, true, &ev));

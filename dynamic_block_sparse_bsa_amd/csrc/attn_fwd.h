@@ -612,6 +612,25 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
 // remapped over the XCDs), or with the stream organization (a separate
 // instantiation, so the one-task kernels keep their register allocation) the
 // workgroup's own run of tasks [seg_ptr[k], seg_ptr[k+1]), one after another.
+// Claim a task from the per-XCD queues (see launch_xq_init): the front of
+// this XCD's queue, else the back of the others' in turn; -1 when all are
+// empty.  Queue y position p is task ((p / C) * 8 + y) * C + p % C.
+__device__ __forceinline__ int claim_task(const AttnArgs& a) {
+  const int C = a.xcd_remap;
+  const unsigned xcc = (unsigned)__builtin_amdgcn_s_getreg(20 | (3 << 11)) & 7u;  // HW_REG_XCC_ID[3:0]
+#pragma unroll 1
+  for (int k = 0; k < 8; ++k) {
+    const unsigned y = (xcc + (unsigned)k) & 7u;
+    const unsigned long long old = atomicAdd(&a.xq[y], k == 0 ? 1ull : 0xffffffff00000000ull);
+    const int head = (int)(uint32_t)old, tail = (int)(uint32_t)(old >> 32);
+    if (head < tail) {
+      const int p = k == 0 ? head : tail - 1;
+      return ((p / C) * 8 + (int)y) * C + p % C;
+    }
+  }
+  return -1;
+}
+
 template <int TQ, int TKV, int D, bool STREAM>
 __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   if constexpr (STREAM) {
@@ -622,18 +641,30 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       attn_task<TQ, TKV, D>(a, a.tasks[t]);
     }
   } else {
-    int bid = blockIdx.x;
-    if (a.xcd_remap > 0) {
-      // Workgroups are dealt to the 8 XCDs round-robin by id.  Remap so that
-      // each XCD receives runs of xcd_remap consecutive tasks (neighbouring
-      // query tiles of a head, which share K/V tiles in that XCD's L2), while
-      // all XCDs still advance through the task list together.
-      const int C = a.xcd_remap;
-      const int s = bid >> 3;
-      bid = (s / C) * (8 * C) + (bid & 7) * C + (s % C);
+    // one task per workgroup: claimed from the per-XCD queues, or by id
+    // (remapped over the XCDs)
+    __shared__ int s_task;
+    int t;
+    if (a.xq) {
+      if (threadIdx.x == 0) s_task = claim_task(a);
+      __syncthreads();
+      t = s_task;
+      if (t < 0) return;
+    } else {
+      int bid = blockIdx.x;
+      if (a.xcd_remap > 0) {
+        // Workgroups are dealt to the 8 XCDs round-robin by id.  Remap so that
+        // each XCD receives runs of xcd_remap consecutive tasks (neighbouring
+        // query tiles of a head, which share K/V tiles in that XCD's L2), while
+        // all XCDs still advance through the task list together.
+        const int C = a.xcd_remap;
+        const int s = bid >> 3;
+        bid = (s / C) * (8 * C) + (bid & 7) * C + (s % C);
+      }
+      if ((unsigned long long)bid >= *a.n_tasks) return;
+      t = bid;
     }
-    if ((unsigned long long)bid >= *a.n_tasks) return;
-    attn_task<TQ, TKV, D>(a, a.tasks[bid]);
+    attn_task<TQ, TKV, D>(a, a.tasks[t]);
   }
 }
 

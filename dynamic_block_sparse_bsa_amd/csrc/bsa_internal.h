@@ -89,6 +89,8 @@ struct AttnArgs {
   int32_t bq;             // B_Q (membership decode when coarsen_q > 1)
   int32_t coarsen_q;
   int32_t xcd_remap;      // > 0: runs of this many consecutive tasks per XCD
+  unsigned long long* xq; // nullable (with xcd_remap): the 8 per-XCD task queues
+                          // (k_xq_init sets them before each launch)
   const int32_t* seg_ptr; // stream organization: workgroup k runs tasks
                           // [seg_ptr[k], seg_ptr[k+1]); nullptr: one task each
   int32_t grid;           // workgroups launched (multiple of 8 * xcd_remap when remapped)
@@ -183,6 +185,19 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
 // (needs each tile row's median column tsig and the tile-list column count
 // ncol).
 constexpr int kSplitRowFactor = 2;
+// Per-XCD task queues of the XCD organizations.  Queue x holds the tasks of
+// runs x, x + 8, x + 16, ... (runs of `run` consecutive tasks), in order; its
+// word is (tail << 32) | head, positions [head, tail) unclaimed.  A workgroup
+// takes the front of its own XCD's queue (atomic add of 1) or, once that is
+// empty, the back of another XCD's queue (atomic add of -1 << 32); a claim is
+// valid iff the returned head < tail, so every task is claimed exactly once
+// and nothing waits.  The XCDs run at different speeds (a few percent apart,
+// the same XCDs from launch to launch), and the fast ones take the slow
+// ones' last tasks.  The launch adds kXcdSpare workgroups per 8 * run tasks
+// (per XCD: one per `run`) so that a fast XCD has workgroups left to steal
+// with; the spare ones that find every queue empty exit.
+constexpr int kXcdSpareDiv = 8;  // spare workgroups: one per kXcdSpareDiv tasks
+hipError_t launch_xq_init(unsigned long long* xq, const unsigned long long* n_tasks, int32_t run, hipStream_t s);
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t split_min, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,

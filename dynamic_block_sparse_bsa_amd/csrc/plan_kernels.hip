@@ -1114,6 +1114,26 @@ hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_h
   return hipGetLastError();
 }
 
+// Queue y of the per-XCD task queues holds the positions of the tasks t <
+// n_tasks with (t / run) % 8 == y: whole rounds of 8 runs give each queue
+// `run` of them, the last partial round what falls in its run.
+__global__ void k_xq_init(unsigned long long* __restrict__ xq, const unsigned long long* __restrict__ n_tasks,
+                          int32_t run) {
+  const int y = threadIdx.x;
+  if (y >= 8) return;
+  const long long n = (long long)*n_tasks;
+  const long long per_round = 8LL * run;
+  const long long rounds = n / per_round, rem = n - rounds * per_round;
+  const long long len = rounds * run + min(max(rem - (long long)y * run, 0LL), (long long)run);
+  atomicExch(&xq[y], (unsigned long long)len << 32);  // head 0, tail len (where the claims' atomics act)
+}
+
+hipError_t launch_xq_init(unsigned long long* xq, const unsigned long long* n_tasks, int32_t run, hipStream_t s) {
+  if (!xq || !n_tasks || run < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_xq_init, dim3(1), dim3(64), 0, s, xq, n_tasks, run);
+  return hipGetLastError();
+}
+
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
                         int32_t refine_q, int32_t split, int32_t split_min, int32_t order, int32_t max_len,
                         int32_t* parts, int32_t* slot_base, Task* tasks, MaskStats* st,
