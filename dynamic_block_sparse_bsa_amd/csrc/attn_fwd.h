@@ -612,20 +612,31 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
 // remapped over the XCDs), or with the stream organization (a separate
 // instantiation, so the one-task kernels keep their register allocation) the
 // workgroup's own run of tasks [seg_ptr[k], seg_ptr[k+1]), one after another.
-// Claim a task from the per-XCD queues (see launch_xq_init): the front of
-// this XCD's queue, else the back of the others' in turn; -1 when all are
-// empty.  Queue y position p is task ((p / C) * 8 + y) * C + p % C.
+// Tasks of queue y (the runs y, y + 8, ... of the XCD organization) with n
+// tasks in all; position p of the queue is task ((p / C) * 8 + y) * C + p % C.
+__device__ __forceinline__ int queue_len(long long n, int C, int y) {
+  const long long rounds = n / (8LL * C), rem = n - rounds * 8LL * C;
+  return (int)(rounds * C + min(max(rem - (long long)y * C, 0LL), (long long)C));
+}
+// The task of this workgroup (see launch_xq_init): in the static prefix of
+// its queue (y = id mod 8, position id / 8) that position; past it, a claim
+// on the front of its own queue's dynamic suffix, else on the back of the
+// other queues' suffixes in turn; -1 when they are all empty.
 __device__ __forceinline__ int claim_task(const AttnArgs& a) {
   const int C = a.xcd_remap;
-  const unsigned xcc = (unsigned)__builtin_amdgcn_s_getreg(20 | (3 << 11)) & 7u;  // HW_REG_XCC_ID[3:0]
+  const long long n = (long long)*a.n_tasks;
+  const int y0 = (int)(blockIdx.x & 7u), k = (int)(blockIdx.x >> 3);
+  const int n0 = queue_len(n, C, y0);
+  if (k < n0 - (n0 >> 3)) return ((k / C) * 8 + y0) * C + k % C;
 #pragma unroll 1
-  for (int k = 0; k < 8; ++k) {
-    const unsigned y = (xcc + (unsigned)k) & 7u;
-    const unsigned long long old = atomicAdd(&a.xq[y], k == 0 ? 1ull : 0xffffffff00000000ull);
+  for (int j = 0; j < 8; ++j) {
+    const int y = (y0 + j) & 7;
+    const int ny = queue_len(n, C, y);
+    const unsigned long long old = atomicAdd(&a.xq[y], j == 0 ? 1ull : 0xffffffff00000000ull);
     const int head = (int)(uint32_t)old, tail = (int)(uint32_t)(old >> 32);
     if (head < tail) {
-      const int p = k == 0 ? head : tail - 1;
-      return ((p / C) * 8 + (int)y) * C + p % C;
+      const int p = ny - (ny >> 3) + (j == 0 ? head : tail - 1);
+      return ((p / C) * 8 + y) * C + p % C;
     }
   }
   return -1;
@@ -641,8 +652,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       attn_task<TQ, TKV, D>(a, a.tasks[t]);
     }
   } else {
-    // one task per workgroup: claimed from the per-XCD queues, or by id
-    // (remapped over the XCDs)
+    // one task per workgroup: by id with the XCD queues' dynamic tails, or
+    // by id (remapped over the XCDs)
     __shared__ int s_task;
     int t;
     if (a.xq) {

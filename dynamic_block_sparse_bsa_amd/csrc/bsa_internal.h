@@ -186,12 +186,15 @@ hipError_t launch_coarsen(const int32_t* row_ptr, const int32_t* cols, int32_t H
 // ncol).
 constexpr int kSplitRowFactor = 2;
 // Per-XCD task queues of the XCD organizations.  Queue x holds the tasks of
-// runs x, x + 8, x + 16, ... (runs of `run` consecutive tasks), in order; its
-// word is (tail << 32) | head, positions [head, tail) unclaimed.  A workgroup
-// takes the front of its own XCD's queue (atomic add of 1) or, once that is
-// empty, the back of another XCD's queue (atomic add of -1 << 32); a claim is
-// valid iff the returned head < tail, so every task is claimed exactly once
-// and nothing waits.  The XCDs run at different speeds (a few percent apart,
+// runs x, x + 8, x + 16, ... (runs of `run` consecutive tasks), in order.
+// Workgroup i (on XCD i mod 8) runs position i / 8 of queue i mod 8 while
+// that lies in the queue's first 7/8 (the static order, which keeps the
+// L2-sharing runs together best).  The last 1/8 of each queue is claimed:
+// its word is (tail << 32) | head over the suffix, positions [head, tail)
+// unclaimed; a workgroup past the prefix takes the front of its own queue's
+// suffix (atomic add of 1) or, once that is empty, the back of another
+// queue's suffix (atomic add of -1 << 32); a claim is valid iff the returned
+// head < tail, so every task runs exactly once and nothing waits.  The XCDs run at different speeds (a few percent apart,
 // the same XCDs from launch to launch), and the fast ones take the slow
 // ones' last tasks.  The launch adds kXcdSpare workgroups per 8 * run tasks
 // (per XCD: one per `run`) so that a fast XCD has workgroups left to steal

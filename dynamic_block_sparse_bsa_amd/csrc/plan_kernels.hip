@@ -1116,7 +1116,8 @@ hipError_t launch_tasks_stream(const int32_t* trow_ptr, int32_t H, int32_t nqt_h
 
 // Queue y of the per-XCD task queues holds the positions of the tasks t <
 // n_tasks with (t / run) % 8 == y: whole rounds of 8 runs give each queue
-// `run` of them, the last partial round what falls in its run.
+// `run` of them, the last partial round what falls in its run.  Its word
+// covers the dynamic suffix, the last len / 8 positions.
 __global__ void k_xq_init(unsigned long long* __restrict__ xq, const unsigned long long* __restrict__ n_tasks,
                           int32_t run) {
   const int y = threadIdx.x;
@@ -1125,7 +1126,8 @@ __global__ void k_xq_init(unsigned long long* __restrict__ xq, const unsigned lo
   const long long per_round = 8LL * run;
   const long long rounds = n / per_round, rem = n - rounds * per_round;
   const long long len = rounds * run + min(max(rem - (long long)y * run, 0LL), (long long)run);
-  atomicExch(&xq[y], (unsigned long long)len << 32);  // head 0, tail len (where the claims' atomics act)
+  // head 0, tail len / 8 (stored by an atomic, where the claims' atomics act)
+  atomicExch(&xq[y], (unsigned long long)(len >> 3) << 32);
 }
 
 hipError_t launch_xq_init(unsigned long long* xq, const unsigned long long* n_tasks, int32_t run, hipStream_t s) {
