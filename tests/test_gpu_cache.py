@@ -92,13 +92,22 @@ def test_plan_cache_ragged_and_unaligned_mask():
         cache.destroy()
 
 
-@pytest.mark.parametrize("force_split", [-1, 1, -2])
-def test_plan_cache_run_speculative(force_split):
+def _xcd_plan(name):
+    return next(e["id"] for e in bsa.catalog() if e["name"] == name)
+
+
+@pytest.mark.parametrize("force_split,plan", [(-1, None), (1, None), (-2, None),
+                                              (-1, "T128x64_d128_splitk_sim_xcd"), (1, "T128x32_d128_splitk_xcd")])
+def test_plan_cache_run_speculative(force_split, plan):
     """bsa_plan_cache_run: the most recently used candidate runs behind the
     comparison, guarded by its verdict.  Every output must match the oracle
     for the mask passed, whether that candidate matched (hit), another one
     did (hit on an older entry) or none did (miss, new plan); force_split=1
-    makes every split-K path (and its merge) part of the guarded run."""
+    makes every split-K path (and its merge) part of the guarded run.  With
+    an XCD organization forced, the guarded runs also go through the per-XCD
+    task queues, which are reset before every launch: a guarded run that must
+    do nothing leaves them empty, and the next run must still cover every
+    task."""
     dev = torch.device("cuda")
     H, N, d, block = 2, 1300, 128, (64, 64)
     masks = []
@@ -113,7 +122,7 @@ def test_plan_cache_run_speculative(force_split):
     def go(i, want_hit):
         out = torch.full(qd.shape, float("nan"), dtype=torch.bfloat16, device=dev)
         o, hit = cache.run(torch.from_numpy(masks[i]).to(dev), block, H, N, d, qd, kd, vd, out,
-                           force_split=force_split)
+                           force_split=force_split, force_plan=_xcd_plan(plan) if plan else -1)
         torch.cuda.synchronize()
         assert hit == want_hit, (i, hit)
         assert_close(o, refs[i], f"mask {i} hit {hit}")
