@@ -149,7 +149,8 @@ bsa_status bsa_plan_create(const bsa_request* req, void* stream, bsa_plan** out)
  * mainloop over the plan's tiles; section 4.3: the split-K merge).  Q, K, V, O are device bf16
  * buffers of batch * H * N * d elements in the request's layout; O is fully
  * written (zeros for empty rows).  Stream-ordered and asynchronous.  One run per plan may be in
- * flight at a time (the split-K workspace is per plan).  Q/K/V may alias each
+ * flight at a time (the split-K workspace and, for the XCD organizations, the
+ * task queues that each run resets are per plan).  Q/K/V may alias each
  * other; O must not alias Q, K or V. */
 bsa_status bsa_run(const bsa_plan* plan, const void* q, const void* k, const void* v, void* o,
                    void* stream);
