@@ -608,10 +608,6 @@ __device__ __forceinline__ void attn_task(const AttnArgs& a, const Task task) {
 #endif
 }
 
-// Task dispatch: one task per workgroup (the task list's order, optionally
-// remapped over the XCDs), or with the stream organization (a separate
-// instantiation, so the one-task kernels keep their register allocation) the
-// workgroup's own run of tasks [seg_ptr[k], seg_ptr[k+1]), one after another.
 // Tasks of queue y (the runs y, y + 8, ... of the XCD organization) with n
 // tasks in all; position p of the queue is task ((p / C) * 8 + y) * C + p % C.
 __device__ __forceinline__ int queue_len(long long n, int C, int y) {
@@ -642,6 +638,12 @@ __device__ __forceinline__ int claim_task(const AttnArgs& a) {
   return -1;
 }
 
+// Task dispatch: one task per workgroup -- in the task list's order, or for
+// the XCD organizations through the per-XCD queues (a static prefix by
+// workgroup id and a claimed tail; claim_task) -- or, with the stream
+// organization (a separate instantiation, so the one-task kernels keep their
+// register allocation), the workgroup's own run of tasks [seg_ptr[k],
+// seg_ptr[k+1]), one after another.
 template <int TQ, int TKV, int D, bool STREAM>
 __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
   if constexpr (STREAM) {
@@ -652,8 +654,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& a) {
       attn_task<TQ, TKV, D>(a, a.tasks[t]);
     }
   } else {
-    // one task per workgroup: by id with the XCD queues' dynamic tails, or
-    // by id (remapped over the XCDs)
+    // one task per workgroup: through the XCD queues, or by id (the static
+    // remap over the XCDs when an XCD organization runs without queues)
     __shared__ int s_task;
     int t;
     if (a.xq) {
