@@ -333,9 +333,10 @@ struct bsa_plan {
   const int32_t* tcol = nullptr;
   const int32_t* tsig = nullptr;  // per tile-list row: the column of its median entry
   const uint32_t* tbits = nullptr;
-  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};  // timing events of bsa_run_timed
-  hipEvent_t done = nullptr;  // recorded after plan creation and after untimed runs
-  hipEvent_t last = nullptr;  // recorded after the plan's latest stream work (done or ev[2])
+  // stream-order bookkeeping, updated by runs of a const plan
+  mutable hipEvent_t ev[3] = {nullptr, nullptr, nullptr};  // timing events of bsa_run_timed (created on first use)
+  hipEvent_t done = nullptr;          // recorded after plan creation and after untimed runs
+  mutable hipEvent_t last = nullptr;  // recorded after the plan's latest stream work (done or ev[2])
 
   hipError_t alloc(size_t bytes, DevBuf* b) {
     return arena ? arena_alloc(arena, dev, bytes, b) : pool_alloc(dev, bytes, b);
@@ -1090,15 +1091,14 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
   a.seg_ptr = p->shape.groups > 0 ? (const int32_t*)p->seg_ptr.ptr : nullptr;
   a.grid = (int32_t)p->grid;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)r.d));
-  bsa_plan* mp = const_cast<bsa_plan*>(p);
   if (a.xq) HIP_TRY(launch_xq_init(a.xq, a.n_tasks, a.xcd_remap, s));
   if (timed) {
-    for (auto& ev : mp->ev)
+    for (auto& ev : p->ev)
       if (!ev) HIP_TRY(event_get(p->dev, true, &ev));
-    HIP_TRY(hipEventRecord(mp->ev[0], s));
+    HIP_TRY(hipEventRecord(p->ev[0], s));
   }
   HIP_TRY(fn(a, (int)p->grid, s));
-  if (timed) HIP_TRY(hipEventRecord(mp->ev[1], s));
+  if (timed) HIP_TRY(hipEventRecord(p->ev[1], s));
   if (p->shape.split > 0 || p->shape.groups > 0) {
     MergeArgs m{};
     m.o = (__bf16*)o;
@@ -1126,18 +1126,18 @@ static bsa_status run_impl(const bsa_plan* p, const void* q, const void* k, cons
     }
     HIP_TRY(launch_merge(m, (int32_t)p->shape.nqt, s, grid_items));
   }
-  if (!timed && mp->done) {
-    HIP_TRY(hipEventRecord(mp->done, s));
-    mp->last = mp->done;
+  if (!timed && p->done) {
+    HIP_TRY(hipEventRecord(p->done, s));
+    p->last = p->done;
   }
   if (timed) {
-    HIP_TRY(hipEventRecord(mp->ev[2], s));
-    mp->last = mp->ev[2];
-    HIP_TRY(hipEventSynchronize(mp->ev[2]));
+    HIP_TRY(hipEventRecord(p->ev[2], s));
+    p->last = p->ev[2];
+    HIP_TRY(hipEventSynchronize(p->ev[2]));
     float t = 0;
-    HIP_TRY(hipEventElapsedTime(&t, mp->ev[0], mp->ev[1]));
+    HIP_TRY(hipEventElapsedTime(&t, p->ev[0], p->ev[1]));
     if (attn_ms) *attn_ms = t;
-    HIP_TRY(hipEventElapsedTime(&t, mp->ev[1], mp->ev[2]));
+    HIP_TRY(hipEventElapsedTime(&t, p->ev[1], p->ev[2]));
     if (merge_ms) *merge_ms = t;
   }
   return BSA_OK;
