@@ -194,11 +194,13 @@ constexpr int kSplitRowFactor = 2;
 // unclaimed; a workgroup past the prefix takes the front of its own queue's
 // suffix (atomic add of 1) or, once that is empty, the back of another
 // queue's suffix (atomic add of -1 << 32); a claim is valid iff the returned
-// head < tail, so every task runs exactly once and nothing waits.  The XCDs run at different speeds (a few percent apart,
-// the same XCDs from launch to launch), and the fast ones take the slow
-// ones' last tasks.  The launch adds kXcdSpare workgroups per 8 * run tasks
-// (per XCD: one per `run`) so that a fast XCD has workgroups left to steal
-// with; the spare ones that find every queue empty exit.
+// head < tail, so every task runs exactly once and nothing waits.  The XCDs
+// run at different speeds (a few percent apart, the same XCDs from launch to
+// launch), and the fast ones take the slow ones' last tasks.  The grid adds
+// one spare workgroup per kXcdSpareDiv tasks (so a fast XCD has workgroups
+// left to steal with; spares that find every queue empty exit) and is
+// rounded up to whole rounds of 8 runs: a queue holds at most grid / 8
+// tasks, so every position of its static prefix has its workgroup.
 constexpr int kXcdSpareDiv = 8;  // spare workgroups: one per kXcdSpareDiv tasks
 hipError_t launch_xq_init(unsigned long long* xq, const unsigned long long* n_tasks, int32_t run, hipStream_t s);
 hipError_t launch_tasks(const int32_t* trow_ptr, int32_t H, int32_t nqt_head, int32_t ntr,
