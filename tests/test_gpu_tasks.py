@@ -17,9 +17,10 @@ checked against the organization's definition:
   them by head, and within a head by non-decreasing band of the median column
   of the query tile's row (8192 / H bands over the row's columns).
 
-The masks are large enough (more than 4096 query tiles) that the task
-builder walks several chunks; sampled output rows of each longest-first plan
-are checked against the oracle.
+Two of the masks are large enough (more than 8192 query tiles for every
+uncoarsened tile shape) that the task builder walks several chunks of its
+counting sort, the third fits one chunk; sampled output rows of each
+longest-first plan are checked against the oracle.
 """
 
 import numpy as np
@@ -75,7 +76,7 @@ def _expected_stream(rp, H, nqb, nqt_head, refine_q, G):
 
 
 # (block, N, H, uncoarsened catalog entries that must be checked)
-CASES = [((64, 64), 40000, 8, 2), ((128, 128), 9000, 6, 6), ((128, 32), 20000, 6, 7)]
+CASES = [((64, 64), 70000, 8, 2), ((128, 128), 9000, 6, 6), ((128, 32), 90000, 12, 7)]
 
 
 @pytest.mark.parametrize("block,N,H,min_checked", CASES)
