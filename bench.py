@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "BSA request latency (ms, incl. planning) + active-block TFLOP/s, bf16 d=128"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 WORKLOAD = {1: "tiny", 2: "medium", 3: "wan720p", 4: "hunyuan", 5: "stream"}
 
 
@@ -258,6 +259,7 @@ def main():
     if args.layout != "HND":
         wl += f", layout {args.layout}"
     planning = [r - a - m for r, a, m in zip(req_ms, attn_ms, merge_ms)]
+    traffic = load_traffic(workload) if args.layout == "HND" else None
     res = {
         "metric": METRIC,
         "value": flops_total / total_s / 1e12,
@@ -284,7 +286,12 @@ def main():
         "regime": info["regime"],
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": load_traffic(workload) if args.layout == "HND" else None},
+                     "traffic": traffic},
+        # the attention kernel's measured HBM bytes per launch (from the
+        # committed counter summary) over its event-timed duration
+        "hbm": None if traffic is None else {
+            "achieved": traffic / (attn_avg * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": traffic / (attn_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS},
     }
     if args.config == 5:
         res["stream"] = {"requests_timed": args.steps, "stream_length": len(reqs),
