@@ -2,9 +2,10 @@
 existing path bsa_plan_create + bsa_run (same request, same inputs), through
 the C ABI: two calls in a row on one device, the second with a smaller input
 (the scratch keeps the first call's contents), each within the parity bar of
-the oracle and of the existing path's output; a request whose block-CSR does
-not fit the fixed scratch is refused with BSA_ERR_UNSUPPORTED and leaves O
-untouched.
+the oracle and of the existing path's output, for the table's plans and for
+every plan of the XCD organizations (per-XCD task queues); a request whose
+block-CSR does not fit the fixed scratch is refused with BSA_ERR_UNSUPPORTED
+and leaves O untouched.
 """
 
 import numpy as np
@@ -68,3 +69,33 @@ def test_oversized_request_refused():
     assert torch.isnan(out).all().item()
     # the scratch still serves a request that fits afterwards
     test_two_calls_match_plan_and_run()
+
+
+def test_xcd_queue_plans():
+    """The XCD organizations dispatch through per-XCD task queues whose words
+    are carved from the scratch as well: every such plan, two calls in a row
+    (the second smaller; fewer tasks than one round of eight runs when the
+    run is 128), against plan + run with the same plan and the oracle."""
+    sizes = [(4, 4096, 128, (128, 32), 51), (2, 1500, 128, (128, 32), 52)]
+    data = []
+    for H, N, d, block, seed in sizes:
+        M, q, k, v = gen.random_case(H, N, d, *block, p=0.25, seed=seed, empty_rows={0: [1]})
+        data.append((M, q, k, v, oatt.attention(q, k, v, M, *block)))
+    H0, N0, d0, b0, _ = sizes[0]
+    ids = [e["id"] for e in bsa.catalog() if e["xcd_remap"] > 0 and bsa.eligible(e["id"], H0, N0, d0, b0)]
+    assert len(ids) >= 4
+    for pid in ids:
+        for (H, N, d, block, _), (M, q, k, v, ref) in zip(sizes, data):
+            where = f"plan {pid} H={H} N={N} d={d} B={block}"
+            p, want = gpu_run(M, q, k, v, block, force_plan=pid)
+            assert p.info["plan_id"] == pid, where
+            p.destroy()
+            dev = torch.device("cuda")
+            Md = torch.from_numpy(np.ascontiguousarray(M)).to(dev)
+            got = torch.full((H, N, d), float("nan"), dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+            bsa.attention_noalloc(Md, block, H, N, d, q.to(dev), k.to(dev), v.to(dev), got, force_plan=pid)
+            torch.cuda.synchronize()
+            assert_close(got, ref, "noalloc " + where)
+            diff = (got.float() - want.float()).abs()
+            assert diff.max().item() <= 1e-2 and diff.mean().item() <= 1e-3, where
